@@ -1,0 +1,154 @@
+"""Planted mistakes in a copy of the oracle must each fail at least one pin.
+
+Each mutant is a one-line edit of ``oracle/hta_oracle.c`` (a dropped term, a wrong index,
+a wrong sign, a transposed operand), compiled with gcc into a temporary directory and
+swapped in for the real library while a fast subset of the pins runs.  The real oracle
+source is never modified.  This shows that the pins are strong enough to catch a
+plausible mistake anywhere in the oracle.
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import bruteforce
+from tree_verification_attention_amd import workloads as W
+
+from helpers import f64, tiny_workload
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "hta_oracle.c")
+
+MUTANTS = {
+    "self_bit_dropped": ("for (int p = i; p != -1; p = par[p])\n                in_tree[p] = 1;",
+                         "for (int p = par[i]; p != -1; p = par[p])\n                in_tree[p] = 1;"),
+    "gqa_mapping_modulo": ("const int g = h / G;", "const int g = h % Hkv;"),
+    "scale_dropped": ("        s *= scale;\n        scores[j] = s;\n        if (s > m)\n            m = s;\n    }\n    /* pass 2",
+                      "        scores[j] = s;\n        if (s > m)\n            m = s;\n    }\n    /* pass 2"),
+    "lse_without_max": ("    *lse = m + log(Z);\n}", "    *lse = log(Z);\n}"),
+    "prefix_off_by_one": ("for (int j = 0; j < prefix_len[b]; ++j)", "for (int j = 1; j < prefix_len[b]; ++j)"),
+    "v_from_k": ("vals[n].base = v_prefix;", "vals[n].base = k_prefix;"),
+    "tree_v_from_k": ("vals[n].base = v_tree;", "vals[n].base = k_tree;"),
+    "q_index_transposed": ("widen(q, (((size_t)b * T + i) * Hq + h) * D + d, is_bf16)",
+                           "widen(q, (((size_t)b * Hq + h) * T + i) * D + d, is_bf16)"),
+    "mask_bit_wrong_node": ("m[p / 64] |= (uint64_t)1 << (p % 64);", "m[p / 64] |= (uint64_t)1 << (i % 64);"),
+    "merge_weight_sign": ("double w = exp(lse_parts[s] - M);", "double w = exp(M - lse_parts[s]);"),
+    "missing_normalisation": ("    for (int d = 0; d < D; ++d)\n        out[d] /= Z;\n    *lse = m + log(Z);\n}",
+                              "    *lse = m + log(Z);\n}"),
+    "exp_sign": ("double p = exp(scores[j] - m);\n        Z += p;\n        for (int d = 0; d < D; ++d)\n            out[d] += p * widen",
+                 "double p = exp(scores[j] + m);\n        Z += p;\n        for (int d = 0; d < D; ++d)\n            out[d] += p * widen"),
+    "tree_keys_wrong_head": ("const size_t base = ((size_t)b * Hkv + g) * (size_t)T * D;",
+                             "const size_t base = ((size_t)b * Hkv + 0) * (size_t)T * D;"),
+}
+
+
+@contextlib.contextmanager
+def swapped(path):
+    old = oracle._lib
+    oracle._lib = oracle.configure(ctypes.CDLL(path))
+    try:
+        yield
+    finally:
+        oracle._lib = old
+
+
+def _bruteforce_pin():
+    gen = torch.Generator().manual_seed(21)
+    for seed in range(3):
+        par = [W.random_forest(6, gen), W.level_tree((2, 2), gen) + [0, 1]]
+        w = tiny_workload(par, B=2, Hq=4, Hkv=2, D=5, L=7, prefix_len=[7, 3], seed=seed,
+                          dtype=torch.bfloat16, peaky=0.3)
+        out, lse = oracle.verify(w.as_numpy(), w.scale)
+        L = lambda t: t.to(torch.float64).tolist()  # noqa: E731
+        bo, bl = bruteforce.verify(L(w.q), L(w.k_prefix), L(w.v_prefix), L(w.k_tree),
+                                   L(w.v_tree), w.parent_idx.tolist(), w.prefix_len.tolist(),
+                                   w.scale)
+        np.testing.assert_allclose(out, np.array(bo), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, np.array(bl), rtol=0, atol=1e-12)
+
+
+def _causal_pin():
+    T, L, G = 5, 9, 2
+    w = tiny_workload(W.chain_tree(T), B=1, Hq=4, Hkv=2, D=8, L=L, seed=3)
+    out, _ = oracle.verify(w.as_numpy(), w.scale)
+    for h in range(4):
+        g = h // G
+        k = torch.cat([f64(w.k_prefix[0, g]), f64(w.k_tree[0, g])])
+        v = torch.cat([f64(w.v_prefix[0, g]), f64(w.v_tree[0, g])])
+        qs = torch.zeros(L + T, 8, dtype=torch.float64)
+        qs[L:] = f64(w.q[0, :, h])
+        ref = F.scaled_dot_product_attention(qs[None], k[None], v[None], is_causal=True,
+                                             scale=w.scale)[0, L:]
+        np.testing.assert_allclose(out[0, :, h], ref.numpy(), rtol=0, atol=1e-12)
+
+
+def _closed_form_pin():
+    par = [-1, 0, 0, 1, 3]
+    w = tiny_workload(par, B=1, Hq=2, Hkv=1, D=3, L=6, seed=4)
+    w.q.zero_()
+    _, lse = oracle.verify(w.as_numpy(), w.scale)
+    dep = W.depths(par)
+    for i in range(5):
+        assert abs(lse[0, 0, i] - math.log(6 + dep[i] + 1)) < 1e-13
+
+
+def _mask_pin():
+    par = np.array([W.chain_tree(70)], dtype=np.int32)
+    masks = oracle.ancestor_masks(par)
+    for i in range(70):
+        full = sum(int(masks[0, i, w]) << (64 * w) for w in range(2))
+        assert full == (1 << (i + 1)) - 1
+
+
+def _merge_pin():
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((1, 4))
+    k = rng.standard_normal((9, 4))
+    v = rng.standard_normal((9, 4))
+    full = np.ones((1, 9), dtype=bool)
+    o_ref, l_ref = oracle.masked_attention(q, k, v, full, 0.5)
+    parts = [np.arange(9) < 4, np.arange(9) >= 4]
+    lp, op = [], []
+    for p in parts:
+        o, l = oracle.masked_attention(q, k, v, full & p[None], 0.5)
+        lp.append(l[0]); op.append(o[0])
+    o, l = oracle.lse_merge(np.array(lp), np.array(op))
+    np.testing.assert_allclose(o, o_ref[0], rtol=0, atol=1e-12)
+    assert abs(l - l_ref[0]) < 1e-12
+
+
+PINS = [_bruteforce_pin, _causal_pin, _closed_form_pin, _mask_pin, _merge_pin]
+
+
+def test_pins_pass_on_the_real_oracle():
+    for pin in PINS:
+        pin()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_each_mutant_fails_a_pin(name, tmp_path):
+    before, after = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(before) >= 1, f"mutation site for {name} not found"
+    mutated = src.replace(before, after, 1)
+    c = tmp_path / "mutant.c"
+    so = tmp_path / "libmutant.so"
+    c.write_text(mutated)
+    subprocess.check_call(["gcc", "-O2", "-fno-fast-math", "-std=c11", "-shared", "-fPIC",
+                           str(c), "-o", str(so), "-lm"])
+    failed = []
+    with swapped(str(so)):
+        for pin in PINS:
+            try:
+                pin()
+            except (AssertionError, oracle.OracleError):
+                failed.append(pin.__name__)
+    assert failed, f"mutant {name} survived every pin"
