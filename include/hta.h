@@ -1,0 +1,183 @@
+/*
+ * hta.h -- C ABI of the MI355X (gfx950) tree verification attention library (libhta.so).
+ *
+ * What the library computes.  LongSpec verifies a speculated draft tree with one target
+ * forward pass whose attention is split in two (LongSpec README, Introduction, "Hybrid
+ * Attention Aggregation"; paper summary, Summary, "Hybrid Tree Attention"; arXiv abstract):
+ * the tree tokens attend to the whole prefix KV cache with no mask, and to each other under
+ * the tree mask; the two partial results are aggregated.  The decoding is lossless (README
+ * title; summary, first paragraph), so the aggregate here is exact: for batch b, query head
+ * h, tree node i, with g = h / (Hq / Hkv),
+ *
+ *     visible(i) = { prefix keys j < prefix_len[b] }  U  { tree node i and its ancestors }
+ *     out[b,i,h,:] = softmax_j( scale * q[b,i,h,:] . k_j ) @ v_j        over j in visible(i)
+ *     lse[b,h,i]   = ln sum_j exp( scale * q[b,i,h,:] . k_j )
+ *
+ * computed as partial attentions over key chunks (split-K over the prefix, one partial for
+ * the tree) merged through their log-sum-exp statistics.
+ *
+ * Layouts (all row-major, contiguous, caller-owned device memory):
+ *     q            [B, T, Hq, D]        in_dtype
+ *     k_prefix     [B, Hkv, Lmax, D]    in_dtype   rows >= prefix_len[b] are never read
+ *     v_prefix     [B, Hkv, Lmax, D]    in_dtype   (they may hold anything, NaN included)
+ *     k_tree       [B, Hkv, T, D]       in_dtype   (q and k arrive already position-encoded)
+ *     v_tree       [B, Hkv, T, D]       in_dtype
+ *     parent_idx   [B, T]   int32       parent of node i, -1 for a child of the prefix;
+ *                                       nodes must be in topological order: parent < i
+ *     prefix_len   [B]      int32       0 <= prefix_len[b] <= Lmax (0 allowed)
+ *     out          [B, T, Hq, D]        float32
+ *     lse          [B, Hq, T]           float32, natural log
+ *     masks        [B, T, ceil(T/64)]   uint64: bit (t % 64) of word t / 64 of node i is set
+ *                                       iff tree node t is i or an ancestor of i
+ *
+ * Ownership and threading.  The library allocates nothing and frees nothing.  Every call
+ * takes a caller-allocated device workspace of at least hta_workspace_size() bytes and a
+ * HIP stream (passed as void*, a hipStream_t; NULL = the default stream).  Calls are
+ * asynchronous: a return of HTA_OK means the work was enqueued on the stream.  The library
+ * keeps no mutable global state beyond a per-device cache of the compute-unit count, so
+ * calls on different streams with different workspaces may run concurrently; calls that
+ * share a workspace must be ordered by the caller.
+ *
+ * Errors.  Every argument check happens on the host before anything is enqueued; on an
+ * error the call returns a non-zero hta_status and enqueues nothing.  Errors only visible on
+ * the device (a parent pointer outside [-1, i-1], a prefix_len outside [0, Lmax]) make the
+ * affected sequence's out and lse rows NaN and are recorded in the workspace; read them
+ * with hta_get_device_status().
+ *
+ * Limits: head_dim in {64, 128}; 1 <= tree_size <= 256; num_q_heads % num_kv_heads == 0;
+ * num_q_heads / num_kv_heads <= 16; every tensor pointer 16-byte aligned, the workspace
+ * 256-byte aligned; in_dtype HTA_BF16.
+ */
+#ifndef HTA_H
+#define HTA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HTA_OK = 0,
+    HTA_ERR_NULL = 1,        /* a required pointer is NULL */
+    HTA_ERR_SHAPE = 2,       /* a size is out of the supported range or inconsistent */
+    HTA_ERR_DTYPE = 3,       /* unsupported in_dtype */
+    HTA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+    HTA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than hta_workspace_size() */
+    HTA_ERR_TREE = 6,        /* (device) a parent pointer outside [-1, i-1] */
+    HTA_ERR_PREFIX_LEN = 7,  /* (device) prefix_len[b] outside [0, max_prefix_len] */
+    HTA_ERR_HIP = 8          /* a HIP runtime call failed */
+} hta_status;
+
+typedef enum { HTA_BF16 = 0, HTA_F32 = 1 } hta_dtype;
+
+/* Problem descriptor.  chunk = 0 lets the library pick the split-K chunk length. */
+typedef struct {
+    int32_t batch;          /* B */
+    int32_t num_q_heads;    /* Hq */
+    int32_t num_kv_heads;   /* Hkv; query head h reads KV head h / (Hq / Hkv) */
+    int32_t head_dim;       /* D, 64 or 128 */
+    int32_t tree_size;      /* T, draft tree nodes per sequence */
+    int32_t max_prefix_len; /* Lmax, the prefix KV cache capacity (row stride of k/v_prefix) */
+    int32_t in_dtype;       /* hta_dtype of q, k_*, v_* */
+    float scale;            /* softmax scale; 0 means 1/sqrt(head_dim) */
+    int32_t chunk;          /* prefix keys per split-K partial (multiple of 64); 0 = auto */
+} hta_desc;
+
+/* How a descriptor is executed; filled by hta_plan().  Sizes in bytes, offsets into the
+ * workspace.  Partial results of split s (s < num_splits: prefix keys
+ * [s*chunk, min((s+1)*chunk, prefix_len[b])); s == num_splits: the tree keys) live at
+ *   lse_part[((b*Hkv + g)*(num_splits+1) + s)*rows_padded + r]              (float)
+ *   o_part  [(((b*Hkv + g)*(num_splits+1) + s)*rows_padded + r)*D + d]      (float)
+ * where row r = i*(Hq/Hkv) + (h % (Hq/Hkv)) packs the query heads sharing KV head g.
+ * o_part holds the normalised partial output, lse_part its natural-log normaliser
+ * (-inf for an empty chunk).  Splits at or past ceil(prefix_len[b]/chunk) are not written. */
+typedef struct {
+    int32_t chunk;          /* prefix keys per split */
+    int32_t num_splits;     /* ceil(max_prefix_len / chunk), at least 1 */
+    int32_t rows;           /* T * Hq / Hkv: query rows per (b, kv head) */
+    int32_t rows_padded;    /* rows rounded up to a multiple of 16 */
+    size_t status_offset;   /* int32 [B]: device status per sequence */
+    size_t masks_offset;    /* uint64 [B, T, ceil(T/64)] */
+    size_t lse_part_offset;
+    size_t o_part_offset;
+    size_t workspace_bytes; /* total, == hta_workspace_size() */
+} hta_plan_info;
+
+/* Fill *info for a descriptor.  Returns HTA_ERR_SHAPE/HTA_ERR_DTYPE/HTA_ERR_NULL on a bad
+ * descriptor. */
+hta_status hta_plan(const hta_desc *desc, hta_plan_info *info);
+
+/* Workspace bytes needed by every entry point for this descriptor (0 if it is invalid). */
+size_t hta_workspace_size(const hta_desc *desc);
+
+/*
+ * The whole verification attention step: ancestor masks, tree partial, split-K prefix
+ * partials, LSE merge -> out, lse.  The exact aggregation of the prefix and tree parts
+ * (README, Introduction; summary, Summary; arXiv abstract).
+ */
+hta_status hta_verify(const hta_desc *desc, const void *q, const void *k_prefix,
+                      const void *v_prefix, const void *k_tree, const void *v_tree,
+                      const int32_t *parent_idx, const int32_t *prefix_len, float *out,
+                      float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Ancestor-or-self masks of every draft tree (the tree mask of README, Introduction),
+ * built on the device from the parent pointers by pointer jumping, into masks (device,
+ * uint64 [B, T, ceil(T/64)]).  An invalid tree is recorded in the workspace status and its
+ * masks are written as all-ones.
+ */
+hta_status hta_ancestor_masks(const hta_desc *desc, const int32_t *parent_idx, uint64_t *masks,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Prefix part only, left as split-K partials in the workspace (layout in hta_plan_info):
+ * the unmasked attention of every tree query over its sequence's prefix keys (summary,
+ * Summary: the prefix pass).  The tree partial slot is not touched.
+ */
+hta_status hta_prefix_partials(const hta_desc *desc, const void *q, const void *k_prefix,
+                               const void *v_prefix, const int32_t *prefix_len, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
+ * Tree part only, left as the partial of slot s = num_splits in the workspace, plus the
+ * ancestor masks in the workspace: tree queries over tree keys under the ancestor-or-self
+ * mask (summary, Summary: the tree pass).  Also records device status.
+ */
+hta_status hta_tree_partials(const hta_desc *desc, const void *q, const void *k_tree,
+                             const void *v_tree, const int32_t *parent_idx,
+                             const int32_t *prefix_len, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
+ * Aggregation only: merge the prefix partials s < ceil(prefix_len[b]/chunk) and the tree
+ * partial found in the workspace into out, lse through their log-sum-exp statistics
+ * (README, Introduction: the aggregation; exact because the decoding is lossless).
+ * include_tree = 0 merges the prefix partials alone (prefix-only attention; an empty
+ * prefix then gives out = 0, lse = -inf).
+ */
+hta_status hta_merge(const hta_desc *desc, const int32_t *prefix_len, int32_t include_tree,
+                     float *out, float *lse, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/*
+ * Synchronise the stream, read the device status the last hta_verify / hta_tree_partials /
+ * hta_ancestor_masks call left in the workspace, and return HTA_OK, HTA_ERR_TREE or
+ * HTA_ERR_PREFIX_LEN (tree errors reported first).  *bad_sequence (if not NULL) receives
+ * the first offending batch index, or -1.
+ */
+hta_status hta_get_device_status(const hta_desc *desc, const void *workspace, void *stream,
+                                 int32_t *bad_sequence);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *hta_status_str(hta_status status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t hta_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HTA_H */

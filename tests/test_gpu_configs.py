@@ -1,0 +1,48 @@
+"""GPU parity on the full-size workloads (Llama-3-8B 32k / 256k, Vicuna-7B batch 8, the QwQ-32B
+decode sweep), in the launch configuration the benchmark times (automatic chunking).
+
+The oracle computes a seeded sample of rows one by one (every sequence's first and last
+rows included); the GPU computes every row, which must all be finite.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from tree_verification_attention_amd import workloads as W
+
+from test_gpu_parity import check_rows, run_gpu, _log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name,rows", [
+    ("llama3_8b_32k", 400),
+    ("llama3_8b_256k", 60),
+    ("vicuna7b_b8", 300),
+])
+def test_config_sampled_rows(name, rows):
+    _log(f"config {name}")
+    w = W.by_name(name)
+    out, lse = run_gpu(w)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    check_rows(w, out, lse, n_rows=rows, seed=1)
+
+
+@pytest.mark.parametrize("prefix", W.QWQ_PREFIXES)
+@pytest.mark.parametrize("chain", [False, True])
+def test_qwq_sweep(prefix, chain):
+    w = W.qwq_32b(prefix, chain=chain)
+    _log(f"config {w.name}")
+    out, lse = run_gpu(w)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    check_rows(w, out, lse, n_rows=200 if prefix >= 16384 else 400, seed=2)
+
+
+def test_tiny_fp32_config():
+    w = W.tiny()
+    if w.dtype == torch.float32:
+        pytest.skip("fp32 inputs are not supported by the bf16 kernels yet")
+    out, lse = run_gpu(w)
+    check_rows(w, out, lse)

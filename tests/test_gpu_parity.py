@@ -1,0 +1,287 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars (bf16 inputs, fp32 accumulation): max |out - oracle| <= 2e-3, max |lse - oracle| <= 1e-3;
+ancestor masks bit-exact.  Every input is seeded and synthetic (tree_verification_attention_amd
+.workloads); the oracle sees exactly the same bits.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tree_verification_attention_amd as hta
+from tree_verification_attention_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 2e-3
+LSE_TOL = 1e-3
+
+
+def _log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(w: W.Workload):
+    d = "cuda"
+    return dict(q=w.q.to(d), k_prefix=w.k_prefix.to(d), v_prefix=w.v_prefix.to(d),
+                k_tree=w.k_tree.to(d), v_tree=w.v_tree.to(d), parent_idx=w.parent_idx.to(d),
+                prefix_len=w.prefix_len.to(d))
+
+
+def run_gpu(w: W.Workload, chunk: int = 0):
+    t = to_dev(w)
+    out, lse = hta.verify(t["q"], t["k_prefix"], t["v_prefix"], t["k_tree"], t["v_tree"],
+                          t["parent_idx"], t["prefix_len"], scale=w.scale, chunk=chunk)
+    torch.cuda.synchronize()
+    return out.cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+def sample_rows(w: W.Workload, n: int, seed: int = 0):
+    B, T, Hq = w.batch, w.tree_size, w.num_q_heads
+    total = B * T * Hq
+    rng = np.random.default_rng(seed)
+    if n >= total:
+        ids = np.arange(total)
+    else:
+        ids = rng.choice(total, size=n, replace=False)
+        # always include the first and last rows of every sequence (ragged edges)
+        extra = [b * T * Hq for b in range(B)] + [(b + 1) * T * Hq - 1 for b in range(B)]
+        ids = np.unique(np.concatenate([ids, extra]))
+    b = ids // (T * Hq)
+    i = (ids // Hq) % T
+    h = ids % Hq
+    return b, h, i
+
+
+def check_rows(w: W.Workload, out, lse, n_rows: int = 10**9, seed: int = 0, part=oracle.PART_ALL,
+               out_tol=OUT_TOL, lse_tol=LSE_TOL):
+    b, h, i = sample_rows(w, n_rows, seed)
+    ro, rl = oracle.rows(w.as_numpy(), w.scale, b, h, i, part)
+    go = out[b, i, h]
+    gl = lse[b, h, i]
+    if part == oracle.PART_PREFIX:
+        empty = np.isneginf(rl)
+        assert np.all(np.isneginf(gl[empty])) and np.all(go[empty] == 0)
+        ro, rl, go, gl = ro[~empty], rl[~empty], go[~empty], gl[~empty]
+    err_o = float(np.max(np.abs(go - ro))) if go.size else 0.0
+    err_l = float(np.max(np.abs(gl - rl))) if gl.size else 0.0
+    _log(f"  [{w.name}] rows={len(b)} max|out-oracle|={err_o:.3e} max|lse-oracle|={err_l:.3e}")
+    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
+    assert err_o <= out_tol, err_o
+    assert err_l <= lse_tol, err_l
+    return err_o, err_l
+
+
+# ----------------------------------------------------------------------------- ancestor masks
+
+
+@pytest.mark.parametrize("T", [1, 5, 7, 63, 64, 65, 68, 130, 256])
+def test_ancestor_masks_bit_exact(T):
+    _log(f"masks T={T}")
+    gen = torch.Generator().manual_seed(100 + T)
+    par = [W.random_forest(T, gen), W.chain_tree(T), W.star_tree(T)]
+    if T == 68:
+        par.append(W.level_tree(W.LONGSPEC_TREE_WIDTHS, gen))
+    pi = torch.tensor(par, dtype=torch.int32)
+    got = hta.ancestor_masks(pi.cuda()).cpu().numpy().view(np.uint64)
+    ref = oracle.ancestor_masks(pi.numpy())
+    np.testing.assert_array_equal(got, ref)
+
+
+# ----------------------------------------------------------------------------- the parts
+
+
+def _small(name, parents, *, B=2, Hq=8, Hkv=2, D=128, L=1000, plen=None, seed=0, peaky=0.02):
+    return W.make_workload(name, batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                           max_prefix_len=L, parents=parents, prefix_len=plen, seed=seed,
+                           peaky_frac=peaky)
+
+
+def test_tree_part_alone_prefix_len_zero():
+    """prefix_len = 0: the whole answer is the tree pass."""
+    gen = torch.Generator().manual_seed(1)
+    par = [W.level_tree(W.LONGSPEC_TREE_WIDTHS, gen) for _ in range(2)]
+    w = _small("tree_only", par, L=128, plen=[0, 0], seed=1)
+    out, lse = run_gpu(w)
+    check_rows(w, out, lse)
+
+
+def test_prefix_partials_match_oracle_per_chunk():
+    """Each split-K partial against the oracle's attention over exactly that key chunk."""
+    gen = torch.Generator().manual_seed(2)
+    par = [W.level_tree(W.LONGSPEC_TREE_WIDTHS, gen) for _ in range(2)]
+    w = _small("chunks", par, L=1000, plen=[1000, 777], seed=2)
+    t = to_dev(w)
+    desc = hta.desc_for(t["q"], t["k_prefix"], w.scale, chunk=256)
+    ws = hta.new_workspace(desc, "cuda")
+    hta.hta_prefix_partials(desc, t["q"], t["k_prefix"], t["v_prefix"], t["prefix_len"], ws)
+    torch.cuda.synchronize()
+    lse_p, o_p = (x.cpu().double().numpy() for x in hta.partial_views(desc, ws))
+    info = hta.plan(desc)
+    G = w.num_q_heads // w.num_kv_heads
+    rng = np.random.default_rng(0)
+    worst_o = worst_l = 0.0
+    for b in range(w.batch):
+        Lb = int(w.prefix_len[b])
+        for s in range((Lb + info.chunk - 1) // info.chunk):
+            k0, k1 = s * info.chunk, min((s + 1) * info.chunk, Lb)
+            for g in range(w.num_kv_heads):
+                K = w.k_prefix[b, g, k0:k1].double().numpy()
+                V = w.v_prefix[b, g, k0:k1].double().numpy()
+                rows = rng.choice(w.tree_size * G, size=24, replace=False)
+                Q = np.stack([w.q[b, r // G, g * G + r % G].double().numpy() for r in rows])
+                ro, rl = oracle.masked_attention(Q, K, V, np.ones((len(rows), k1 - k0), bool),
+                                                 w.scale)
+                worst_o = max(worst_o, float(np.max(np.abs(o_p[b, g, s, rows] - ro))))
+                worst_l = max(worst_l, float(np.max(np.abs(lse_p[b, g, s, rows] - rl))))
+    _log(f"  per-chunk partials: max|o|={worst_o:.3e} max|lse|={worst_l:.3e}")
+    assert worst_o <= OUT_TOL and worst_l <= LSE_TOL
+
+
+def test_merge_matches_oracle_merge_of_gpu_partials():
+    """lse_merge against the oracle's merge applied to the very partials the GPU produced."""
+    gen = torch.Generator().manual_seed(3)
+    par = [W.level_tree(W.LONGSPEC_TREE_WIDTHS, gen) for _ in range(2)]
+    w = _small("merge", par, L=1000, plen=[1000, 321], seed=3)
+    t = to_dev(w)
+    desc = hta.desc_for(t["q"], t["k_prefix"], w.scale, chunk=128)
+    ws = hta.new_workspace(desc, "cuda")
+    hta.hta_tree_partials(desc, t["q"], t["k_tree"], t["v_tree"], t["parent_idx"],
+                          t["prefix_len"], ws)
+    hta.hta_prefix_partials(desc, t["q"], t["k_prefix"], t["v_prefix"], t["prefix_len"], ws)
+    B, T, Hq, D = w.q.shape
+    out = torch.empty(B, T, Hq, D, device="cuda")
+    lse = torch.empty(B, Hq, T, device="cuda")
+    hta.hta_merge(desc, t["prefix_len"], True, out, lse, ws)
+    torch.cuda.synchronize()
+    lse_p, o_p = (x.cpu().double().numpy() for x in hta.partial_views(desc, ws))
+    info = hta.plan(desc)
+    out, lse = out.cpu().double().numpy(), lse.cpu().double().numpy()
+    G = Hq // w.num_kv_heads
+    worst = 0.0
+    for b in range(B):
+        n = (int(w.prefix_len[b]) + info.chunk - 1) // info.chunk
+        slots = list(range(n)) + [info.num_splits]
+        for i in range(0, T, 5):
+            for h in range(Hq):
+                g, r = h // G, i * G + h % G
+                ro, rl = oracle.lse_merge(lse_p[b, g, slots, r], o_p[b, g, slots, r])
+                worst = max(worst, float(np.max(np.abs(out[b, i, h] - ro))),
+                            abs(lse[b, h, i] - rl))
+    _log(f"  merge vs oracle merge of the same partials: {worst:.3e}")
+    assert worst <= 1e-5
+
+
+# ----------------------------------------------------------------------------- whole step
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 4, 5, 8])
+def test_verify_small_shapes(D, G):
+    gen = torch.Generator().manual_seed(10 * G + D)
+    par = [W.level_tree(W.LONGSPEC_TREE_WIDTHS, gen), W.random_forest(68, gen)]
+    w = _small(f"small_D{D}_G{G}", par, B=2, Hq=2 * G, Hkv=2, D=D, L=1100, plen=[1100, 613],
+               seed=G + D)
+    _log(f"verify small D={D} G={G}")
+    out, lse = run_gpu(w)
+    check_rows(w, out, lse)
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 130, 256])
+def test_verify_tree_sizes(T):
+    gen = torch.Generator().manual_seed(T)
+    par = [W.chain_tree(T), W.random_forest(T, gen)]
+    w = _small(f"T{T}", par, B=2, Hq=4, Hkv=1, D=128, L=300, plen=[300, 65], seed=T)
+    _log(f"verify T={T}")
+    out, lse = run_gpu(w)
+    check_rows(w, out, lse, n_rows=4000)
+
+
+@pytest.mark.parametrize("chunk", [64, 192, 1024, 4096])
+def test_verify_chunk_sizes_all_within_tolerance(chunk):
+    gen = torch.Generator().manual_seed(7)
+    par = [W.level_tree(W.LONGSPEC_TREE_WIDTHS, gen)]
+    w = _small("chunks", par, B=1, Hq=8, Hkv=2, L=3000, plen=[2999], seed=7)
+    out, lse = run_gpu(w, chunk=chunk)
+    check_rows(w, out, lse, n_rows=2000)
+
+
+def test_empty_and_tiny_prefixes():
+    gen = torch.Generator().manual_seed(8)
+    par = [W.level_tree((2, 3), gen) for _ in range(4)]
+    w = _small("edge_prefix", par, B=4, Hq=4, Hkv=2, L=70, plen=[0, 1, 63, 70], seed=8)
+    out, lse = run_gpu(w)
+    check_rows(w, out, lse)
+
+
+def test_empty_cache_capacity():
+    w = _small("lmax0", [W.chain_tree(5)], B=1, Hq=4, Hkv=2, L=0, plen=[0], seed=9)
+    out, lse = run_gpu(w)
+    check_rows(w, out, lse)
+
+
+def test_nan_padding_is_never_read():
+    w = W.make_workload("poison", batch=3, num_q_heads=4, num_kv_heads=2, head_dim=128,
+                        max_prefix_len=700, prefix_len=[700, 300, 5],
+                        tree_widths=W.LONGSPEC_TREE_WIDTHS, poison_padding=True, seed=11)
+    out, lse = run_gpu(w)
+    check_rows(w, out, lse)
+
+
+def test_bitwise_deterministic():
+    w = W.llama3_8b(4096, seed=5)
+    a = run_gpu(w)
+    b = run_gpu(w)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+# ----------------------------------------------------------------------------- device errors
+
+
+def test_invalid_tree_is_flagged_and_poisons_only_its_sequence():
+    gen = torch.Generator().manual_seed(12)
+    good = W.level_tree((2, 3), gen)
+    bad = list(good)
+    bad[3] = 4  # parent after the child
+    w = _small("badtree", [good, bad], B=2, Hq=4, Hkv=2, L=100, seed=12)
+    t = to_dev(w)
+    desc = hta.desc_for(t["q"], t["k_prefix"], w.scale)
+    ws = hta.new_workspace(desc, "cuda")
+    B, T, Hq, D = w.q.shape
+    out = torch.empty(B, T, Hq, D, device="cuda")
+    lse = torch.empty(B, Hq, T, device="cuda")
+    hta.hta_verify(desc, t["q"], t["k_prefix"], t["v_prefix"], t["k_tree"], t["v_tree"],
+                   t["parent_idx"], t["prefix_len"], out, lse, ws)
+    code, seq = hta.hta_get_device_status(desc, ws)
+    assert code == 6 and seq == 1
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(np.isnan(o[1])) and np.all(np.isnan(l[1]))
+    assert np.all(np.isfinite(o[0])) and np.all(np.isfinite(l[0]))
+    # a later good call clears the status
+    t["parent_idx"][1] = torch.tensor(good, dtype=torch.int32)
+    hta.hta_verify(desc, t["q"], t["k_prefix"], t["v_prefix"], t["k_tree"], t["v_tree"],
+                   t["parent_idx"], t["prefix_len"], out, lse, ws)
+    assert hta.hta_get_device_status(desc, ws) == (0, -1)
+
+
+def test_prefix_len_out_of_range_is_flagged():
+    w = _small("badlen", [W.chain_tree(3)] * 2, B=2, Hq=2, Hkv=1, L=64, seed=13)
+    t = to_dev(w)
+    t["prefix_len"] = torch.tensor([64, 65], dtype=torch.int32, device="cuda")
+    desc = hta.desc_for(t["q"], t["k_prefix"], w.scale)
+    ws = hta.new_workspace(desc, "cuda")
+    out = torch.empty(2, 3, 2, 128, device="cuda")
+    lse = torch.empty(2, 2, 3, device="cuda")
+    hta.hta_verify(desc, t["q"], t["k_prefix"], t["v_prefix"], t["k_tree"], t["v_tree"],
+                   t["parent_idx"], t["prefix_len"], out, lse, ws)
+    code, seq = hta.hta_get_device_status(desc, ws)
+    assert code == 7 and seq == 1
+    assert np.all(np.isnan(out[1].cpu().numpy())) and np.all(np.isfinite(out[0].cpu().numpy()))

@@ -1,0 +1,32 @@
+"""MI355X-native tree verification attention (LongSpec's Hybrid Tree Attention).
+
+The compute path is ``libhta.so``: hand-written gfx950 HIP kernels behind the C ABI of
+``include/hta.h``.  ``binding`` is its thin ctypes binding (same entry-point names);
+``workloads`` draws the seeded synthetic inputs.  The shared library is loaded on first
+use and its absence is an error -- there is no CPU fallback.
+"""
+from .binding import (  # noqa: F401
+    HtaError,
+    ancestor_masks,
+    desc_for,
+    hta_ancestor_masks,
+    hta_get_device_status,
+    hta_merge,
+    hta_prefix_partials,
+    hta_tree_partials,
+    hta_verify,
+    load,
+    make_desc,
+    new_workspace,
+    partial_views,
+    plan,
+    status_str,
+    verify,
+    workspace_size,
+)
+
+__all__ = [
+    "HtaError", "ancestor_masks", "desc_for", "hta_ancestor_masks", "hta_get_device_status",
+    "hta_merge", "hta_prefix_partials", "hta_tree_partials", "hta_verify", "load", "make_desc",
+    "new_workspace", "partial_views", "plan", "status_str", "verify", "workspace_size",
+]

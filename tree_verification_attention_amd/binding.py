@@ -1,0 +1,268 @@
+"""ctypes binding of libhta.so (the C ABI in include/hta.h).
+
+Argument marshalling only: every step of the verification attention runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory (tensors, the workspace) and the
+stream.  If the shared library has not been built, loading raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhta.so")
+
+HTA_BF16, HTA_F32 = 0, 1
+
+STATUS_NAMES = {
+    0: "HTA_OK",
+    1: "HTA_ERR_NULL",
+    2: "HTA_ERR_SHAPE",
+    3: "HTA_ERR_DTYPE",
+    4: "HTA_ERR_ALIGN",
+    5: "HTA_ERR_WORKSPACE",
+    6: "HTA_ERR_TREE",
+    7: "HTA_ERR_PREFIX_LEN",
+    8: "HTA_ERR_HIP",
+}
+EXPORTED = (
+    "hta_plan",
+    "hta_workspace_size",
+    "hta_verify",
+    "hta_ancestor_masks",
+    "hta_prefix_partials",
+    "hta_tree_partials",
+    "hta_merge",
+    "hta_get_device_status",
+    "hta_status_str",
+    "hta_version",
+)
+
+
+class HtaError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        self.code = code
+        name = status_str(code) if _lib is not None else STATUS_NAMES.get(code, str(code))
+        super().__init__(f"{what}: {name}" if what else name)
+
+
+class hta_desc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("tree_size", ctypes.c_int32),
+        ("max_prefix_len", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("chunk", ctypes.c_int32),
+    ]
+
+
+class hta_plan_info(ctypes.Structure):
+    _fields_ = [
+        ("chunk", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("rows", ctypes.c_int32),
+        ("rows_padded", ctypes.c_int32),
+        ("status_offset", ctypes.c_size_t),
+        ("masks_offset", ctypes.c_size_t),
+        ("lse_part_offset", ctypes.c_size_t),
+        ("o_part_offset", ctypes.c_size_t),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libhta.so (raises if it is missing: the HIP path is the only path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -m tree_verification_attention_amd.build`"
+        )
+    L = ctypes.CDLL(path)
+    P, S, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    D = ctypes.POINTER(hta_desc)
+    L.hta_plan.argtypes = [D, ctypes.POINTER(hta_plan_info)]
+    L.hta_workspace_size.argtypes = [D]
+    L.hta_workspace_size.restype = S
+    L.hta_verify.argtypes = [D, P, P, P, P, P, P, P, P, P, P, S, P]
+    L.hta_ancestor_masks.argtypes = [D, P, P, P, S, P]
+    L.hta_prefix_partials.argtypes = [D, P, P, P, P, P, S, P]
+    L.hta_tree_partials.argtypes = [D, P, P, P, P, P, P, S, P]
+    L.hta_merge.argtypes = [D, P, I, P, P, P, S, P]
+    L.hta_get_device_status.argtypes = [D, P, P, ctypes.POINTER(ctypes.c_int32)]
+    L.hta_status_str.argtypes = [ctypes.c_int]
+    L.hta_status_str.restype = ctypes.c_char_p
+    L.hta_version.argtypes = []
+    for f in (L.hta_plan, L.hta_verify, L.hta_ancestor_masks, L.hta_prefix_partials,
+              L.hta_tree_partials, L.hta_merge, L.hta_get_device_status, L.hta_version):
+        f.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_str(code: int) -> str:
+    return load().hta_status_str(int(code)).decode()
+
+
+def _check(code: int, what: str) -> None:
+    if code != 0:
+        raise HtaError(code, what)
+
+
+def make_desc(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, tree_size: int,
+              max_prefix_len: int, in_dtype: int = HTA_BF16, scale: float = 0.0,
+              chunk: int = 0) -> hta_desc:
+    return hta_desc(batch, num_q_heads, num_kv_heads, head_dim, tree_size, max_prefix_len,
+                    in_dtype, float(scale), chunk)
+
+
+def plan(desc: hta_desc) -> hta_plan_info:
+    info = hta_plan_info()
+    _check(load().hta_plan(ctypes.byref(desc), ctypes.byref(info)), "hta_plan")
+    return info
+
+
+def workspace_size(desc: hta_desc) -> int:
+    return int(load().hta_workspace_size(ctypes.byref(desc)))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return HTA_BF16
+    if t.dtype == torch.float32:
+        return HTA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def desc_for(q: torch.Tensor, k_prefix: torch.Tensor, scale: Optional[float] = None,
+             chunk: int = 0) -> hta_desc:
+    B, T, Hq, D = q.shape
+    Hkv, Lmax = k_prefix.shape[1], k_prefix.shape[2]
+    return make_desc(B, Hq, Hkv, D, T, Lmax, _dtype_code(q), 0.0 if scale is None else scale,
+                     chunk)
+
+
+def new_workspace(desc: hta_desc, device) -> torch.Tensor:
+    n = workspace_size(desc)
+    if n == 0:
+        _check(2, "hta_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _contig(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+# ----------------------------------------------------------------------------- entry points
+
+
+def hta_verify(desc, q, k_prefix, v_prefix, k_tree, v_tree, parent_idx, prefix_len, out, lse,
+               workspace, stream=None) -> None:
+    _contig(q, k_prefix, v_prefix, k_tree, v_tree, parent_idx, prefix_len, out, lse, workspace)
+    _check(load().hta_verify(ctypes.byref(desc), _ptr(q), _ptr(k_prefix), _ptr(v_prefix),
+                             _ptr(k_tree), _ptr(v_tree), _ptr(parent_idx), _ptr(prefix_len),
+                             _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                             _stream(stream)), "hta_verify")
+
+
+def hta_ancestor_masks(desc, parent_idx, masks, workspace, stream=None) -> None:
+    _contig(parent_idx, masks, workspace)
+    _check(load().hta_ancestor_masks(ctypes.byref(desc), _ptr(parent_idx), _ptr(masks),
+                                     _ptr(workspace), workspace.numel(), _stream(stream)),
+           "hta_ancestor_masks")
+
+
+def hta_prefix_partials(desc, q, k_prefix, v_prefix, prefix_len, workspace, stream=None) -> None:
+    _contig(q, k_prefix, v_prefix, prefix_len, workspace)
+    _check(load().hta_prefix_partials(ctypes.byref(desc), _ptr(q), _ptr(k_prefix),
+                                      _ptr(v_prefix), _ptr(prefix_len), _ptr(workspace),
+                                      workspace.numel(), _stream(stream)),
+           "hta_prefix_partials")
+
+
+def hta_tree_partials(desc, q, k_tree, v_tree, parent_idx, prefix_len, workspace,
+                      stream=None) -> None:
+    _contig(q, k_tree, v_tree, parent_idx, prefix_len, workspace)
+    _check(load().hta_tree_partials(ctypes.byref(desc), _ptr(q), _ptr(k_tree), _ptr(v_tree),
+                                    _ptr(parent_idx), _ptr(prefix_len), _ptr(workspace),
+                                    workspace.numel(), _stream(stream)), "hta_tree_partials")
+
+
+def hta_merge(desc, prefix_len, include_tree: bool, out, lse, workspace, stream=None) -> None:
+    _contig(prefix_len, out, lse, workspace)
+    _check(load().hta_merge(ctypes.byref(desc), _ptr(prefix_len), 1 if include_tree else 0,
+                            _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                            _stream(stream)), "hta_merge")
+
+
+def hta_get_device_status(desc, workspace, stream=None) -> Tuple[int, int]:
+    bad = ctypes.c_int32(-1)
+    code = load().hta_get_device_status(ctypes.byref(desc), _ptr(workspace), _stream(stream),
+                                        ctypes.byref(bad))
+    return int(code), int(bad.value)
+
+
+# ----------------------------------------------------------------------------- convenience
+
+
+def verify(q, k_prefix, v_prefix, k_tree, v_tree, parent_idx, prefix_len, *, scale=None,
+           chunk: int = 0, workspace: Optional[torch.Tensor] = None, stream=None
+           ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Tree verification attention on device tensors: returns (out fp32 [B,T,Hq,D],
+    lse fp32 [B,Hq,T]).  A workspace is allocated through torch if none is given."""
+    desc = desc_for(q, k_prefix, scale, chunk)
+    B, T, Hq, D = q.shape
+    out = torch.empty(B, T, Hq, D, dtype=torch.float32, device=q.device)
+    lse = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(desc, q.device)
+    hta_verify(desc, q, k_prefix, v_prefix, k_tree, v_tree, parent_idx, prefix_len, out, lse,
+               workspace, stream)
+    return out, lse
+
+
+def ancestor_masks(parent_idx: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """Packed ancestor-or-self masks uint64 [B, T, ceil(T/64)] (as int64 storage)."""
+    B, T = parent_idx.shape
+    desc = make_desc(B, 1, 1, 64, T, 0)
+    W = (T + 63) // 64
+    masks = torch.empty(B, T, W, dtype=torch.int64, device=parent_idx.device)
+    if workspace is None:
+        workspace = new_workspace(desc, parent_idx.device)
+    hta_ancestor_masks(desc, parent_idx, masks, workspace, stream)
+    return masks
+
+
+def partial_views(desc: hta_desc, workspace: torch.Tensor):
+    """(lse_part [B,Hkv,S+1,R_pad], o_part [B,Hkv,S+1,R_pad,D]) views of a workspace."""
+    p = plan(desc)
+    B, Hkv, D = desc.batch, desc.num_kv_heads, desc.head_dim
+    S1, Rp = p.num_splits + 1, p.rows_padded
+    n = B * Hkv * S1 * Rp
+    lse = workspace[p.lse_part_offset:p.lse_part_offset + 4 * n].view(torch.float32)
+    o = workspace[p.o_part_offset:p.o_part_offset + 4 * n * D].view(torch.float32)
+    return lse.view(B, Hkv, S1, Rp), o.view(B, Hkv, S1, Rp, D)

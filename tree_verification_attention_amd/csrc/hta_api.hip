@@ -1,0 +1,272 @@
+// hta_api.hip -- the C ABI of libhta.so (declared in include/hta.h): argument checking,
+// planning (split-K chunk, workspace carve-up) and the kernel launch sequence.
+//
+// Nothing here allocates device memory: the caller hands in the workspace.  All checks run
+// on the host before the first launch, so a rejected call enqueues nothing.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/hta.h"
+#include "hta_internal.h"
+
+using hta::Geometry;
+using hta::Workspace;
+
+namespace {
+
+// The split-K chunk is sized so one (sequence, KV head, row block) pass over the prefix
+// spreads across the chip's compute units.  A fixed count keeps plans (and workspace
+// sizes) independent of which device is current; MI355X has 256 CUs.
+constexpr int64_t kPlanCUs = 256;
+constexpr int kMinChunk = 256;
+constexpr int kMaxChunk = 8192;
+constexpr int kMaxTree = 256;
+constexpr int kMaxGroup = 16;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+hta_status make_plan(const hta_desc* d, Geometry* g, hta_plan_info* info) {
+  if (!d) return HTA_ERR_NULL;
+  if (d->in_dtype != HTA_BF16) return HTA_ERR_DTYPE;
+  if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->tree_size < 1 ||
+      d->tree_size > kMaxTree || d->max_prefix_len < 0 ||
+      (d->head_dim != 64 && d->head_dim != 128) || d->num_q_heads % d->num_kv_heads != 0 ||
+      d->num_q_heads / d->num_kv_heads > kMaxGroup || !(d->scale >= 0.f) || isinf(d->scale) ||
+      d->chunk < 0 || d->chunk % 64 != 0)
+    return HTA_ERR_SHAPE;
+  Geometry G;
+  G.B = d->batch;
+  G.T = d->tree_size;
+  G.Hq = d->num_q_heads;
+  G.Hkv = d->num_kv_heads;
+  G.D = d->head_dim;
+  G.Lmax = d->max_prefix_len;
+  G.G = G.Hq / G.Hkv;
+  G.R = G.T * G.G;
+  G.R_pad = (G.R + 15) / 16 * 16;
+  G.NT = G.R_pad / 16;
+  G.W = (G.T + 63) / 64;
+  G.scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)G.D);
+  const int mt = hta::prefix_tiles_per_wave(G);
+  const int64_t row_blocks = (G.NT + 4 * mt - 1) / (4 * mt);
+  int64_t chunk = d->chunk;
+  if (chunk == 0) {
+    // Batches may be ragged (prefix_len varies); smaller chunks then balance the load.
+    const int64_t waves = G.B > 1 ? 4 : 1;
+    const int64_t work = (int64_t)G.B * G.Hkv * row_blocks * (int64_t)G.Lmax;
+    chunk = (work + kPlanCUs * waves - 1) / (kPlanCUs * waves);
+    chunk = (chunk + 63) / 64 * 64;
+    if (chunk < kMinChunk) chunk = kMinChunk;
+    if (chunk > kMaxChunk) chunk = kMaxChunk;
+  }
+  G.chunk = (int32_t)chunk;
+  int64_t S = (G.Lmax + chunk - 1) / chunk;
+  if (S < 1) S = 1;
+  if (S > (1 << 20)) return HTA_ERR_SHAPE;
+  G.S = (int32_t)S;
+
+  hta_plan_info p;
+  memset(&p, 0, sizeof p);
+  p.chunk = G.chunk;
+  p.num_splits = G.S;
+  p.rows = G.R;
+  p.rows_padded = G.R_pad;
+  size_t off = 0;
+  p.status_offset = off;
+  off = round_up(off + sizeof(int32_t) * (size_t)G.B, 256);
+  p.masks_offset = off;
+  off = round_up(off + sizeof(uint64_t) * (size_t)G.B * G.T * G.W, 256);
+  const size_t parts = (size_t)G.B * G.Hkv * (size_t)(G.S + 1) * G.R_pad;
+  p.lse_part_offset = off;
+  off = round_up(off + sizeof(float) * parts, 256);
+  p.o_part_offset = off;
+  off = round_up(off + sizeof(float) * parts * G.D, 256);
+  p.workspace_bytes = off;
+  if (g) *g = G;
+  if (info) *info = p;
+  return HTA_OK;
+}
+
+Workspace carve(void* base, const hta_plan_info& p) {
+  char* c = (char*)base;
+  Workspace w;
+  w.status = (int32_t*)(c + p.status_offset);
+  w.masks = (uint64_t*)(c + p.masks_offset);
+  w.lse_part = (float*)(c + p.lse_part_offset);
+  w.o_part = (float*)(c + p.o_part_offset);
+  return w;
+}
+
+hta_status check_ws(const hta_plan_info& p, const void* ws, size_t bytes) {
+  if (!ws || bytes < p.workspace_bytes) return HTA_ERR_WORKSPACE;
+  if (((uintptr_t)ws & 255u) != 0) return HTA_ERR_ALIGN;
+  return HTA_OK;
+}
+
+hta_status check_ptrs(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (!p) return HTA_ERR_NULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return HTA_ERR_ALIGN;
+  return HTA_OK;
+}
+
+hta_status hip_status(hipError_t e) { return e == hipSuccess ? HTA_OK : HTA_ERR_HIP; }
+
+#define HTA_TRY(expr)                  \
+  do {                                 \
+    hta_status _s = (expr);            \
+    if (_s != HTA_OK) return _s;       \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+hta_status hta_plan(const hta_desc* desc, hta_plan_info* info) {
+  if (!info) return HTA_ERR_NULL;
+  return make_plan(desc, nullptr, info);
+}
+
+size_t hta_workspace_size(const hta_desc* desc) {
+  hta_plan_info p;
+  if (make_plan(desc, nullptr, &p) != HTA_OK) return 0;
+  return p.workspace_bytes;
+}
+
+hta_status hta_verify(const hta_desc* desc, const void* q, const void* k_prefix,
+                      const void* v_prefix, const void* k_tree, const void* v_tree,
+                      const int32_t* parent_idx, const int32_t* prefix_len, float* out,
+                      float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry G;
+  hta_plan_info p;
+  HTA_TRY(make_plan(desc, &G, &p));
+  HTA_TRY(check_ptrs({q, k_tree, v_tree, parent_idx, prefix_len, out, lse}));
+  if (G.Lmax > 0) HTA_TRY(check_ptrs({k_prefix, v_prefix}));  // an empty cache is never read
+  HTA_TRY(check_ws(p, workspace, workspace_bytes));
+  const Workspace ws = carve(workspace, p);
+  hipStream_t s = (hipStream_t)stream;
+  HTA_TRY(hip_status(hta::launch_tree_attn_masked(G, q, k_tree, v_tree, parent_idx, prefix_len,
+                                                  ws, ws.masks, true, s)));
+  HTA_TRY(hip_status(
+      hta::launch_prefix_attn_splitk(G, q, k_prefix, v_prefix, prefix_len, ws, 256, s)));
+  return hip_status(hta::launch_lse_merge(G, prefix_len, true, out, lse, ws, s));
+}
+
+hta_status hta_ancestor_masks(const hta_desc* desc, const int32_t* parent_idx, uint64_t* masks,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry G;
+  hta_plan_info p;
+  HTA_TRY(make_plan(desc, &G, &p));
+  if (!parent_idx || !masks) return HTA_ERR_NULL;
+  if (!aligned16(parent_idx) || !aligned16(masks)) return HTA_ERR_ALIGN;
+  HTA_TRY(check_ws(p, workspace, workspace_bytes));
+  const Workspace ws = carve(workspace, p);
+  // masks-only mode: no attention, prefix_len not read (status records tree validity only)
+  return hip_status(hta::launch_tree_attn_masked(G, nullptr, nullptr, nullptr, parent_idx,
+                                                 nullptr, ws, masks, false,
+                                                 (hipStream_t)stream));
+}
+
+hta_status hta_prefix_partials(const hta_desc* desc, const void* q, const void* k_prefix,
+                               const void* v_prefix, const int32_t* prefix_len, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  Geometry G;
+  hta_plan_info p;
+  HTA_TRY(make_plan(desc, &G, &p));
+  HTA_TRY(check_ptrs({q, prefix_len}));
+  if (G.Lmax > 0) HTA_TRY(check_ptrs({k_prefix, v_prefix}));
+  HTA_TRY(check_ws(p, workspace, workspace_bytes));
+  const Workspace ws = carve(workspace, p);
+  return hip_status(hta::launch_prefix_attn_splitk(G, q, k_prefix, v_prefix, prefix_len, ws, 256,
+                                                   (hipStream_t)stream));
+}
+
+hta_status hta_tree_partials(const hta_desc* desc, const void* q, const void* k_tree,
+                             const void* v_tree, const int32_t* parent_idx,
+                             const int32_t* prefix_len, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  Geometry G;
+  hta_plan_info p;
+  HTA_TRY(make_plan(desc, &G, &p));
+  HTA_TRY(check_ptrs({q, k_tree, v_tree, parent_idx, prefix_len}));
+  HTA_TRY(check_ws(p, workspace, workspace_bytes));
+  const Workspace ws = carve(workspace, p);
+  return hip_status(hta::launch_tree_attn_masked(G, q, k_tree, v_tree, parent_idx, prefix_len, ws,
+                                                 ws.masks, true, (hipStream_t)stream));
+}
+
+hta_status hta_merge(const hta_desc* desc, const int32_t* prefix_len, int32_t include_tree,
+                     float* out, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  Geometry G;
+  hta_plan_info p;
+  HTA_TRY(make_plan(desc, &G, &p));
+  HTA_TRY(check_ptrs({prefix_len, out, lse}));
+  HTA_TRY(check_ws(p, workspace, workspace_bytes));
+  const Workspace ws = carve(workspace, p);
+  return hip_status(hta::launch_lse_merge(G, prefix_len, include_tree != 0, out, lse, ws,
+                                          (hipStream_t)stream));
+}
+
+hta_status hta_get_device_status(const hta_desc* desc, const void* workspace, void* stream,
+                                 int32_t* bad_sequence) {
+  Geometry G;
+  hta_plan_info p;
+  HTA_TRY(make_plan(desc, &G, &p));
+  if (bad_sequence) *bad_sequence = -1;
+  if (!workspace) return HTA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t host_status[1024];
+  hta_status first_tree = HTA_OK, first_len = HTA_OK;
+  int32_t bad_tree = -1, bad_len = -1;
+  for (int b0 = 0; b0 < G.B; b0 += 1024) {
+    const int n = G.B - b0 < 1024 ? G.B - b0 : 1024;
+    const char* src = (const char*)workspace + p.status_offset + sizeof(int32_t) * (size_t)b0;
+    if (hipMemcpyAsync(host_status, src, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost, s) !=
+            hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return HTA_ERR_HIP;
+    for (int k = 0; k < n; ++k) {
+      if ((host_status[k] & hta::kStatusTree) && first_tree == HTA_OK) {
+        first_tree = HTA_ERR_TREE;
+        bad_tree = b0 + k;
+      }
+      if ((host_status[k] & hta::kStatusPrefixLen) && first_len == HTA_OK) {
+        first_len = HTA_ERR_PREFIX_LEN;
+        bad_len = b0 + k;
+      }
+    }
+  }
+  if (first_tree != HTA_OK) {
+    if (bad_sequence) *bad_sequence = bad_tree;
+    return first_tree;
+  }
+  if (first_len != HTA_OK) {
+    if (bad_sequence) *bad_sequence = bad_len;
+    return first_len;
+  }
+  return HTA_OK;
+}
+
+const char* hta_status_str(hta_status status) {
+  switch (status) {
+    case HTA_OK: return "HTA_OK";
+    case HTA_ERR_NULL: return "HTA_ERR_NULL: a required pointer is NULL";
+    case HTA_ERR_SHAPE: return "HTA_ERR_SHAPE: unsupported or inconsistent sizes";
+    case HTA_ERR_DTYPE: return "HTA_ERR_DTYPE: unsupported input dtype";
+    case HTA_ERR_ALIGN: return "HTA_ERR_ALIGN: pointer not 16-byte aligned (workspace: 256)";
+    case HTA_ERR_WORKSPACE: return "HTA_ERR_WORKSPACE: workspace missing or too small";
+    case HTA_ERR_TREE: return "HTA_ERR_TREE: a parent pointer lies outside [-1, i-1]";
+    case HTA_ERR_PREFIX_LEN: return "HTA_ERR_PREFIX_LEN: prefix_len outside [0, max_prefix_len]";
+    case HTA_ERR_HIP: return "HTA_ERR_HIP: a HIP runtime call failed";
+  }
+  return "HTA_ERR_UNKNOWN";
+}
+
+int32_t hta_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// hta_internal.h -- shared declarations of the gfx950 kernels and their host launchers.
+//
+// Everything here is private to libhta.so; the public C ABI is include/hta.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hta {
+
+// Operand types of the CDNA4 bf16 matrix-core instructions.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Device status codes, one int32 per sequence in the workspace.
+constexpr int32_t kStatusTree = 1;       // a parent pointer outside [-1, i-1]
+constexpr int32_t kStatusPrefixLen = 2;  // prefix_len[b] outside [0, Lmax]
+
+// Geometry shared by every kernel of one call (a plain struct passed by value).
+struct Geometry {
+  int32_t B, T, Hq, Hkv, D, Lmax;
+  int32_t G;            // Hq / Hkv: query heads per KV head
+  int32_t R;            // T * G query rows per (b, kv head)
+  int32_t R_pad;        // R rounded up to 16
+  int32_t NT;           // R_pad / 16 row tiles
+  int32_t W;            // ceil(T / 64) mask words per node
+  int32_t chunk;        // prefix keys per split
+  int32_t S;            // number of prefix splits (the tree partial is slot S)
+  float scale;          // softmax scale
+};
+
+struct Workspace {
+  int32_t* status;      // [B]
+  uint64_t* masks;      // [B, T, W]
+  float* lse_part;      // [B, Hkv, S+1, R_pad]
+  float* o_part;        // [B, Hkv, S+1, R_pad, D]
+};
+
+// Host launchers (each enqueues exactly one kernel on the stream).
+hipError_t launch_prefix_attn_splitk(const Geometry& g, const void* q, const void* k_prefix,
+                                     const void* v_prefix, const int32_t* prefix_len,
+                                     const Workspace& ws, int cu_count, hipStream_t stream);
+hipError_t launch_tree_attn_masked(const Geometry& g, const void* q, const void* k_tree,
+                                   const void* v_tree, const int32_t* parent_idx,
+                                   const int32_t* prefix_len, const Workspace& ws,
+                                   uint64_t* masks_out, bool attention, hipStream_t stream);
+hipError_t launch_lse_merge(const Geometry& g, const int32_t* prefix_len, bool include_tree,
+                            float* out, float* lse, const Workspace& ws, hipStream_t stream);
+
+// Row tiles a prefix workgroup's four waves cover (MT tiles per wave, 4*MT per block).
+int prefix_tiles_per_wave(const Geometry& g);
+
+}  // namespace hta
