@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of one tree-verification-attention step on one MI355X.
+
+A step is one ``hta_verify`` call: ancestor masks + tree pass, split-K prefix pass, LSE
+merge -- the whole verification attention of one layer -- on the Llama-3-8B layer shape
+with a 32k-token prefix and the 68-node LongSpec draft tree (4,16,16,16,16).  Inputs are
+seeded synthetic tensors already resident in HBM.  To time HBM rather than the 256 MB
+Infinity Cache, consecutive steps rotate over copies of the prefix KV cache totalling at
+least 1 GiB.
+
+Prints ONE JSON line: the step time (us/step) plus, for the dominant kernel
+(prefix_attn_splitk), its roofline figures measured live with HIP events around launches
+of that kernel alone, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import tree_verification_attention_amd as hta  # noqa: E402
+from tree_verification_attention_amd import workloads as W  # noqa: E402
+
+METRIC = "verification-attention µs/step + achieved HBM GB/s, Llama-3-8B shape, 32k prefix"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix, published
+ROTATE_BYTES = 1 << 30
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "tree_verification_attention_amd", "csrc",
+                          "prefix_attn_splitk.hip")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def alg_figures(w: W.Workload):
+    """Algorithmic bytes and flops of one step and of the prefix kernel alone.
+
+    Per KV head and prefix key the prefix pass must read 2*D*2 bytes of K and V (bf16) and
+    performs 4*D*T*G flops (QK^T and PV for all T*G query rows that share the head).
+    """
+    B, T, Hq, D = w.q.shape
+    Hkv = w.num_kv_heads
+    G = Hq // Hkv
+    el = w.q.element_size()
+    sum_L = int(w.prefix_len.sum())
+    depths = [W.depths(p) for p in w.parent_idx.tolist()]
+    vis_tree = sum(sum(d) + len(d) for d in depths)  # sum over nodes of (depth + 1)
+    kv_bytes = 2 * Hkv * sum_L * D * el
+    q_bytes = B * T * Hq * D * el
+    prefix_bytes = kv_bytes + q_bytes
+    prefix_flops = 4 * D * G * T * Hkv * sum_L
+    step_bytes = (prefix_bytes + 2 * B * Hkv * T * D * el + B * T * 4
+                  + B * T * Hq * D * 4 + B * Hq * T * 4 + B * 4)
+    step_flops = prefix_flops + 4 * D * Hq * vis_tree
+    return dict(step_bytes=step_bytes, step_flops=step_flops, prefix_bytes=prefix_bytes,
+                prefix_flops=prefix_flops, kv_bytes_per_unit=2 * D * el,
+                kv_units=Hkv * sum_L)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM traffic of the prefix kernel from committed rocprofv3 counter runs, only if they
+    were taken on the current kernel source."""
+    p = os.path.join(PROFILE_DIR, f"prefix_attn_splitk_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w: W.Workload, max_seconds: float = 12.0):
+    """Time the oracle (single-threaded fp64 C) on a bounded row sample, scaled per step."""
+    import oracle  # test infrastructure: only this baseline leg uses it
+    a = w.as_numpy()
+    B, T, Hq = w.batch, w.tree_size, w.num_q_heads
+    total = B * T * Hq
+    rng = np.random.default_rng(0)
+    # calibrate with a few rows, then size the sample to the time budget
+    rb, ri, rh = [0] * 8, list(range(8)), [0] * 8
+    t0 = time.perf_counter()
+    oracle.rows(a, w.scale, rb, rh, ri)
+    per_row = (time.perf_counter() - t0) / 8
+    n = int(min(total, max(16, max_seconds / max(per_row, 1e-9))))
+    ids = np.sort(rng.choice(total, size=n, replace=False))
+    b, i, h = ids // (T * Hq), (ids // Hq) % T, ids % Hq
+    t0 = time.perf_counter()
+    oracle.rows(a, w.scale, b, h, i)
+    dt = time.perf_counter() - t0
+    us_per_step = dt / n * total * 1e6
+    return {"value": us_per_step, "unit": "µs/step", "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {total} query rows (b, head, node) of the same workload, "
+                      f"single-threaded fp64 C oracle, {dt:.1f} s, scaled to the full step"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama3_8b_32k", choices=W.CONFIG_NAMES)
+    ap.add_argument("--chunk", type=int, default=0, help="split-K chunk (0 = library default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", default="bench", choices=["bench", "prefix-only", "copy"],
+                    help="prefix-only / copy: launch only that kernel (for counter runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this path runs on one GPU (the work shards by KV head with no "
+              "communication); run with --gpus 1", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    hta.load()
+
+    if args.mode == "copy":
+        # plain copy of known size: calibrates the FETCH_SIZE / WRITE_SIZE counters
+        n = 256 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n,
+                          "launches": args.warmup + args.steps}))
+        return 0
+
+    log(f"[bench] workload {args.workload}: generating inputs")
+    w = W.by_name(args.workload)
+    fig = alg_figures(w)
+    B, T, Hq, D = w.q.shape
+    kv_copy_bytes = w.k_prefix.numel() * w.k_prefix.element_size() * 2
+    n_copies = max(1, min(16, math.ceil(ROTATE_BYTES / kv_copy_bytes)))
+    q = w.q.to(dev)
+    kt, vt = w.k_tree.to(dev), w.v_tree.to(dev)
+    par, plen = w.parent_idx.to(dev), w.prefix_len.to(dev)
+    kp0, vp0 = w.k_prefix.to(dev), w.v_prefix.to(dev)
+    kps = [kp0] + [kp0.clone() for _ in range(n_copies - 1)]
+    vps = [vp0] + [vp0.clone() for _ in range(n_copies - 1)]
+    desc = hta.desc_for(q, kp0, w.scale, args.chunk)
+    info = hta.plan(desc)
+    ws = hta.new_workspace(desc, dev)
+    out = torch.empty(B, T, Hq, D, dtype=torch.float32, device=dev)
+    lse = torch.empty(B, Hq, T, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    log(f"[bench] chunk {info.chunk}, splits {info.num_splits}, rows {info.rows}, "
+        f"{n_copies} KV copies of {kv_copy_bytes / 1e6:.1f} MB")
+
+    def step(k):
+        hta.hta_verify(desc, q, kps[k % n_copies], vps[k % n_copies], kt, vt, par, plen, out,
+                       lse, ws, stream)
+
+    def prefix_only(k):
+        hta.hta_prefix_partials(desc, q, kps[k % n_copies], vps[k % n_copies], plen, ws, stream)
+
+    if args.mode == "prefix-only":
+        for k in range(args.warmup + args.steps):
+            prefix_only(k)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "prefix-only", "workload": args.workload,
+                          "launches": args.warmup + args.steps,
+                          "alg_bytes_per_launch": fig["prefix_bytes"]}))
+        return 0
+
+    # ---- whole step
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    code, _ = hta.hta_get_device_status(desc, ws, stream)
+    if code != 0:
+        raise RuntimeError(f"device status {hta.status_str(code)}")
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us_per_step = wall / args.steps * 1e6
+    log(f"[bench] step: {us_per_step:.2f} us")
+
+    # ---- dominant kernel alone, HIP events on the launch stream
+    for k in range(args.warmup):
+        prefix_only(k)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(args.steps):
+        prefix_only(k)
+    e1.record(stream)
+    e1.synchronize()
+    prefix_us = e0.elapsed_time(e1) / args.steps * 1e3
+    achieved_gbs = fig["prefix_bytes"] / (prefix_us * 1e-6) / 1e9
+    achieved_tflops = fig["prefix_flops"] / (prefix_us * 1e-6) / 1e12
+    log(f"[bench] prefix_attn_splitk: {prefix_us:.2f} us, {achieved_gbs:.0f} GB/s, "
+        f"{achieved_tflops:.0f} TFLOP/s")
+
+    # ---- the other two kernels alone (context for the step time)
+    e0.record(stream)
+    for k in range(args.steps):
+        hta.hta_tree_partials(desc, q, kt, vt, par, plen, ws, stream)
+    e1.record(stream)
+    e1.synchronize()
+    tree_us = e0.elapsed_time(e1) / args.steps * 1e3
+    e0.record(stream)
+    for k in range(args.steps):
+        hta.hta_merge(desc, plen, True, out, lse, ws, stream)
+    e1.record(stream)
+    e1.synchronize()
+    merge_us = e0.elapsed_time(e1) / args.steps * 1e3
+    log(f"[bench] tree_attn_masked: {tree_us:.2f} us, lse_merge: {merge_us:.2f} us")
+
+    result = {
+        "metric": METRIC,
+        "value": round(us_per_step, 3),
+        "unit": "µs/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_per_step / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": B, "num_q_heads": Hq, "num_kv_heads": w.num_kv_heads, "head_dim": D,
+            "prefix_len": int(w.prefix_len.max()), "tree_nodes": T,
+            "tree_widths": list(W.LONGSPEC_TREE_WIDTHS), "chunk": info.chunk,
+            "splits": info.num_splits, "kv_copies_rotated": n_copies,
+        },
+        "step": {
+            "alg_bytes": fig["step_bytes"], "alg_flops": fig["step_flops"],
+            "achieved_GBps": round(fig["step_bytes"] / (us_per_step * 1e-6) / 1e9, 1),
+            "roofline_frac": round(max(fig["step_bytes"] / (HBM_PEAK_GBS * 1e9),
+                                       fig["step_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+                                   / (us_per_step * 1e-6), 4),
+            "kernel_us": {"prefix_attn_splitk": round(prefix_us, 3),
+                          "tree_attn_masked": round(tree_us, 3),
+                          "lse_merge": round(merge_us, 3)},
+        },
+        "roofline": {
+            "kernel": "prefix_attn_splitk",
+            "bound": "hbm",
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic(w.name),
+            "alg_bytes_per_launch": fig["prefix_bytes"],
+            "kernel_us": round(prefix_us, 3),
+            "mfma": {"achieved": round(achieved_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,153 @@
+"""Host-side contract of libhta.so (no GPU needed).
+
+The library must load on a machine without a GPU, export every entry point that
+include/hta.h declares, and reject bad arguments on the host, before any HIP call, with
+the documented status codes.  Pointers below are fake non-null addresses: every case here
+fails validation, so nothing is ever dereferenced or launched.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import tree_verification_attention_amd as hta
+from tree_verification_attention_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hta.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE = 0, 1, 2, 3, 4, 5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(hta_[a-z_]+)\s*\(", text,
+                                 re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = hta.load()
+    names = declared_functions()
+    assert "hta_verify" in names and len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in include/hta.h but not exported"
+    assert set(names) == set(B.EXPORTED)
+
+
+def test_status_strings_cover_every_code():
+    for code, name in B.STATUS_NAMES.items():
+        assert hta.status_str(code).startswith(name)
+    assert hta.status_str(99) == "HTA_ERR_UNKNOWN"
+
+
+def _desc(**kw):
+    base = dict(batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, tree_size=68,
+                max_prefix_len=32768)
+    base.update(kw)
+    return B.make_desc(**base)
+
+
+def _plan_code(d):
+    info = B.hta_plan_info()
+    return hta.load().hta_plan(ctypes.byref(d), ctypes.byref(info))
+
+
+def test_plan_llama_shape():
+    p = hta.plan(_desc())
+    assert p.rows == 272 and p.rows_padded == 272
+    assert p.num_splits * p.chunk >= 32768 and p.chunk % 64 == 0
+    assert p.workspace_bytes == hta.workspace_size(_desc())
+    # partial buffers hold (splits + 1) slots: the last one is the tree partial
+    n = 8 * (p.num_splits + 1) * 272
+    assert p.o_part_offset >= p.lse_part_offset + 4 * n
+    assert p.workspace_bytes >= p.o_part_offset + 4 * n * 128
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), SHAPE),
+    (dict(head_dim=256), SHAPE),
+    (dict(num_q_heads=30), SHAPE),          # not a multiple of num_kv_heads
+    (dict(num_q_heads=8 * 17), SHAPE),      # group of 17 > 16
+    (dict(tree_size=0), SHAPE),
+    (dict(tree_size=257), SHAPE),
+    (dict(batch=0), SHAPE),
+    (dict(max_prefix_len=-1), SHAPE),
+    (dict(chunk=100), SHAPE),               # not a multiple of 64
+    (dict(scale=-1.0), SHAPE),
+    (dict(scale=float("nan")), SHAPE),
+    (dict(in_dtype=1), DTYPE),
+    (dict(in_dtype=7), DTYPE),
+])
+def test_bad_descriptors_are_rejected(kw, code):
+    d = _desc(**kw)
+    assert _plan_code(d) == code
+    assert hta.workspace_size(d) == 0
+
+
+def test_null_descriptor():
+    L = hta.load()
+    info = B.hta_plan_info()
+    assert L.hta_plan(None, ctypes.byref(info)) == NULL
+    assert L.hta_workspace_size(None) == 0
+
+
+FAKE = 0x10000  # 64 KiB-aligned fake device address; never dereferenced
+
+
+def _verify_code(d, ptrs=None, ws=FAKE, ws_bytes=None):
+    p = [FAKE] * 9 if ptrs is None else ptrs
+    if ws_bytes is None:
+        ws_bytes = max(hta.workspace_size(d), 1)
+    return hta.load().hta_verify(ctypes.byref(d), *p, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("i", range(9))
+def test_verify_rejects_each_null_pointer(i):
+    p = [FAKE] * 9
+    p[i] = None
+    assert _verify_code(_desc(), p) == NULL
+
+
+@pytest.mark.parametrize("i", range(9))
+def test_verify_rejects_each_misaligned_pointer(i):
+    p = [FAKE] * 9
+    p[i] = FAKE + 8
+    assert _verify_code(_desc(), p) == ALIGN
+
+
+def test_verify_workspace_checks():
+    d = _desc()
+    n = hta.workspace_size(d)
+    assert _verify_code(d, ws=None) == WORKSPACE
+    assert _verify_code(d, ws_bytes=n - 1) == WORKSPACE
+    assert _verify_code(d, ws=FAKE + 16) == ALIGN
+
+
+def test_empty_cache_allows_null_prefix_pointers_in_validation():
+    # with max_prefix_len = 0 the prefix pointers are never read; validation then only
+    # fails on the workspace (the fake workspace size is too small on purpose)
+    d = _desc(max_prefix_len=0)
+    p = [FAKE] * 9
+    p[1] = p[2] = None
+    assert _verify_code(d, p, ws_bytes=1) == WORKSPACE
+
+
+def test_other_entry_points_validate_before_launching():
+    L = hta.load()
+    d = _desc()
+    n = hta.workspace_size(d)
+    assert L.hta_prefix_partials(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, n, None) == NULL
+    assert L.hta_prefix_partials(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, n - 1, None) == WORKSPACE
+    assert L.hta_tree_partials(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, n, None) == NULL
+    assert L.hta_merge(ctypes.byref(d), FAKE, 1, FAKE, FAKE + 4, FAKE, n, None) == ALIGN
+    assert L.hta_ancestor_masks(ctypes.byref(d), FAKE, None, FAKE, n, None) == NULL
+    bad = _desc(head_dim=80)
+    assert L.hta_merge(ctypes.byref(bad), FAKE, 1, FAKE, FAKE, FAKE, n, None) == SHAPE
+    assert L.hta_get_device_status(ctypes.byref(d), None, None, None) == WORKSPACE
+
+
+def test_version():
+    assert hta.load().hta_version() >= 100

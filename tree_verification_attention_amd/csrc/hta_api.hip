@@ -50,8 +50,9 @@ hta_status make_plan(const hta_desc* d, Geometry* g, hta_plan_info* info) {
   G.NT = G.R_pad / 16;
   G.W = (G.T + 63) / 64;
   G.scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)G.D);
-  const int mt = hta::prefix_tiles_per_wave(G);
-  const int64_t row_blocks = (G.NT + 4 * mt - 1) / (4 * mt);
+  int mt, tpb, nb;
+  hta::prefix_row_blocking(G, &mt, &tpb, &nb);
+  const int64_t row_blocks = nb;
   int64_t chunk = d->chunk;
   if (chunk == 0) {
     // Batches may be ragged (prefix_len varies); smaller chunks then balance the load.
@@ -152,7 +153,7 @@ hta_status hta_verify(const hta_desc* desc, const void* q, const void* k_prefix,
   HTA_TRY(hip_status(hta::launch_tree_attn_masked(G, q, k_tree, v_tree, parent_idx, prefix_len,
                                                   ws, ws.masks, true, s)));
   HTA_TRY(hip_status(
-      hta::launch_prefix_attn_splitk(G, q, k_prefix, v_prefix, prefix_len, ws, 256, s)));
+      hta::launch_prefix_attn_splitk(G, q, k_prefix, v_prefix, prefix_len, ws, s)));
   return hip_status(hta::launch_lse_merge(G, prefix_len, true, out, lse, ws, s));
 }
 
@@ -181,7 +182,7 @@ hta_status hta_prefix_partials(const hta_desc* desc, const void* q, const void* 
   if (G.Lmax > 0) HTA_TRY(check_ptrs({k_prefix, v_prefix}));
   HTA_TRY(check_ws(p, workspace, workspace_bytes));
   const Workspace ws = carve(workspace, p);
-  return hip_status(hta::launch_prefix_attn_splitk(G, q, k_prefix, v_prefix, prefix_len, ws, 256,
+  return hip_status(hta::launch_prefix_attn_splitk(G, q, k_prefix, v_prefix, prefix_len, ws,
                                                    (hipStream_t)stream));
 }
 

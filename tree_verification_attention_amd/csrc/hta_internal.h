@@ -46,7 +46,7 @@ struct Workspace {
 // Host launchers (each enqueues exactly one kernel on the stream).
 hipError_t launch_prefix_attn_splitk(const Geometry& g, const void* q, const void* k_prefix,
                                      const void* v_prefix, const int32_t* prefix_len,
-                                     const Workspace& ws, int cu_count, hipStream_t stream);
+                                     const Workspace& ws, hipStream_t stream);
 hipError_t launch_tree_attn_masked(const Geometry& g, const void* q, const void* k_tree,
                                    const void* v_tree, const int32_t* parent_idx,
                                    const int32_t* prefix_len, const Workspace& ws,
@@ -54,7 +54,8 @@ hipError_t launch_tree_attn_masked(const Geometry& g, const void* q, const void*
 hipError_t launch_lse_merge(const Geometry& g, const int32_t* prefix_len, bool include_tree,
                             float* out, float* lse, const Workspace& ws, hipStream_t stream);
 
-// Row tiles a prefix workgroup's four waves cover (MT tiles per wave, 4*MT per block).
-int prefix_tiles_per_wave(const Geometry& g);
+// How the prefix pass blocks the query rows of one KV head: mt full row tiles per wave,
+// tiles_per_block row tiles per workgroup, blocks workgroups per (sequence, KV head, chunk).
+void prefix_row_blocking(const Geometry& g, int* mt, int* tiles_per_block, int* blocks);
 
 }  // namespace hta
