@@ -213,6 +213,30 @@ def test_verify_chunk_sizes_all_within_tolerance(chunk):
     check_rows(w, out, lse, n_rows=2000)
 
 
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 8, 8), (128, 20, 4)])
+def test_late_score_spikes(D, Hq, Hkv):
+    """Keys far above every score of their chunk's first 32 keys (the prefix pass must not
+    saturate its fp16 probabilities): keys equal to a multiple of one query's vector, placed
+    early, mid-chunk and in a chunk's last tile, for rows of full and leftover row tiles."""
+    gen = torch.Generator().manual_seed(21)
+    par = [W.level_tree(W.LONGSPEC_TREE_WIDTHS, gen)]
+    w = _small(f"spikes_D{D}", par, B=1, Hq=Hq, Hkv=Hkv, D=D, L=3000, plen=[2990], seed=21,
+               peaky=0.0)
+    G = Hq // Hkv
+    T = w.tree_size
+    # (key position, query node, head in group, factor): score ~ factor * |q|^2 * scale
+    spikes = [(5, 0, 0, 1.5), (700, T - 1, G - 1, 2.0), (1024 + 40, T // 2, 0, 3.0),
+              (2047, T - 2, G // 2, 2.5), (2960, 3, G - 1, 2.0)]
+    for g in range(Hkv):
+        for pos, node, hg, f in spikes:
+            qv = w.q[0, node, g * G + hg].float()
+            w.k_prefix[0, g, pos] = (f * qv).to(w.k_prefix.dtype)
+    _log(f"late spikes D={D} Hq={Hq} Hkv={Hkv}")
+    for chunk in (1024, 0):
+        out, lse = run_gpu(w, chunk=chunk)
+        check_rows(w, out, lse)
+
+
 def test_empty_and_tiny_prefixes():
     gen = torch.Generator().manual_seed(8)
     par = [W.level_tree((2, 3), gen) for _ in range(4)]

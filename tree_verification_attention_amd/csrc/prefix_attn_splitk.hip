@@ -10,55 +10,78 @@
 //
 // MI355X mapping
 //  * GQA packing: the T*G query rows sharing KV head g (row r = node*G + head-in-group) are
-//    processed together, so each K/V byte leaves HBM once per chunk and feeds 4*T*G flops.
+//    processed by one workgroup, so each K/V byte leaves HBM once per chunk and feeds
+//    4*T*G flops.
 //  * Matrix cores: scores are formed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16;
 //    A = 16 keys x 32 dims from LDS, B = 16 query rows kept in registers), and the output
 //    transposed too, O^T += V^T P^T (v_mfma_f32_16x16x32_f16).  With both products
 //    transposed, the lane holding score column "row" of S^T is the lane holding operand
 //    column "row" of P^T and output column "row" of O^T: the softmax needs no data movement
-//    between the products and its rescale factors are lane-local.  V^T operands come from
-//    V kept row-major in LDS through the transposing read ds_read_b64_tr_b16.
-//  * Load balance: the row tiles of a block are dealt to the four waves (one per SIMD);
-//    when their count is not a multiple of four, the leftover tiles are split over the
-//    waves by key sub-blocks instead, and the waves' partial results for them are merged
-//    through LDS at the end, so every SIMD does the same matrix work.
+//    between the products and its rescale factors are lane-local.
+//  * Two waves per SIMD (8 per workgroup), in two groups (waves 0-3 and 4-7, one of each
+//    per SIMD).  A wave's own VALU work overlaps its matrix-core work poorly, but the VALU
+//    work of one wave overlaps the MFMAs of the other, so the second group runs one step
+//    behind the first: while one wave of a SIMD computes its softmax, the other feeds the
+//    matrix core.  Each wave holds MT row tiles.  Leftover tiles (when the count is not a
+//    multiple of 8) go to the second group, split by output dimensions: each of its waves
+//    forms the leftover scores and writes its own slice of d.  The first group instead
+//    streams the tiles and builds V^T, so both groups carry similar work per tile.
 //  * Memory: K and V tiles of 64 keys stream HBM -> LDS with direct LDS loads
-//    (global_load_lds_dwordx4, no register staging) through a 4-stage ring, three tiles in
-//    flight while one is consumed; rows are stored unpadded with an XOR swizzle of their
-//    16-byte chunks so the operand reads and the transposing reads are conflict-free.  Keys
-//    past the chunk end re-read the last valid key (never the padding) and are masked.
-//  * Softmax in fp32 with exp2 (scale*log2(e) folded into one FMA).  The running maximum is
-//    only raised when some score exceeds it by more than 2^8 (a wave-wide ballot), so the
-//    accumulator rescale and the cross-lane maximum leave the common path; the result is
-//    exact either way, since numerator and normaliser share the reference.  Probabilities
-//    enter the PV product as fp16 (nearest-even, 11 significant bits), V is widened from
-//    bf16 to fp16 in registers (exact for |v| in [2^-14, 65504]), and the normaliser sums
-//    the unrounded fp32 probabilities.
+//    (global_load_lds_dwordx4, no register staging), two to three tiles in flight while
+//    one is consumed.  Rows land unpadded with an XOR swizzle of their 16-byte chunks so
+//    operand reads are bank-conflict-free.  Keys past the chunk end re-read the last valid
+//    key (never the padding) and are masked.
+//  * V^T operand: once per tile the first group turns the landed bf16 V tile into an fp16
+//    V^T tile (transposing reads ds_read_b64_tr_b16, widening in registers, one 16-byte
+//    store per lane) laid out in the exact key order of the P^T operand, so the PV product
+//    reads plain conflict-free 16-byte operands.  This runs one tile ahead of the compute.
+//  * Softmax in fp32 with exp2 (scale*log2(e) folded into one FMA) against a per-row
+//    reference: the maximum of the chunk's first 32 keys, raised only when a lane's
+//    probabilities of a 32-key half sum above 2^8 (a wave-wide ballot), so the accumulator
+//    rescale leaves the common path; the result is exact either way, since numerator and
+//    normaliser share the reference.  Probabilities enter the PV product as fp16
+//    (nearest-even, 11 significant bits, at most 2^8), V is widened from bf16 to fp16
+//    (exact for |v| in [2^-14, 65504]), and the normaliser sums the unrounded fp32
+//    probabilities.
 #include "hta_internal.h"
+
+#include <type_traits>
 
 namespace hta {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kKeyTile = 64;
-constexpr int kStages = 4;
-constexpr float kRescaleSlack = 8.f;  // log2 units: probabilities stay below 2^8
+constexpr int kKStages = 4;  // K ring: tile t (scores), t+1 (landed), t+2, t+3 (in flight)
+constexpr int kVStages = 3;  // V ring: tile t+1 (being transposed), t+2, t+3 (in flight)
+constexpr int kVtStages = 3;  // V^T: tiles t-1 (second wave group), t (consumed), t+1 (made)
+// instruction classes of the scheduling hints (__builtin_amdgcn_sched_group_barrier masks)
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr float kRaiseP = 256.f;  // probabilities stay below 2^8 (fp16 max 65504)
 
 template <int D>
 struct Layout {
   static constexpr int kRowBytes = D * 2;
-  static constexpr int kChunks = D / 8;                          // 16-byte chunks per row
-  static constexpr int kTileBytes = kKeyTile * kRowBytes;        // one K or V tile
-  static constexpr int kStageBytes = 2 * kTileBytes;
-  static constexpr int kDmaPerWave = kTileBytes / (kWaves * 1024);  // per tensor per tile
+  static constexpr int kChunks = D / 8;                             // 16-byte chunks per row
+  static constexpr int kTileBytes = kKeyTile * kRowBytes;           // one K, V or V^T tile
+  // the first wave group (4 waves) streams the tiles and builds V^T
+  static constexpr int kDmaPerWave = kTileBytes / (4 * 1024);  // per tensor per tile
+  static constexpr int kKRing = 0;
+  static constexpr int kVRing = kKStages * kTileBytes;
+  static constexpr int kVt = kVRing + kVStages * kTileBytes;
+  static constexpr int kBytes = kVt + kVtStages * kTileBytes;
 };
 
-// XOR swizzles of the 16-byte chunk index within a row: K rows are read 16 at a time at
-// one chunk column (D = 128: chunk ^ row%16 spreads the 16 rows over all 64 banks), V rows
-// 4 at a time over two chunk columns by the transposing read (chunk ^ 2*(row%8) keeps the
-// 4 rows x 2 chunks of one 16-lane block on distinct banks).
+// XOR swizzles of the 16-byte chunk index within a row.
+//  K rows (D bf16) are read 16 at a time at one chunk column: D = 128 uses chunk ^ row%16,
+//    which spreads the 16 rows over all 64 banks.
+//  V rows (D bf16) are read 4 at a time over two chunk columns by the transposing read:
+//    chunk ^ 2*(row%8) keeps the 4 rows x 2 chunks of one 16-lane block on distinct banks.
+//  V^T rows (one per d, 64 keys fp16 = 8 chunks) are read 16 at a time at one chunk column:
+//    chunk ^ (row/2)%8 (rows 2m and 2m+1 sit in opposite bank halves).
 template <int D>
 __device__ __forceinline__ int swz_k(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
@@ -67,6 +90,7 @@ template <int D>
 __device__ __forceinline__ int swz_v(int row) {
   return D == 128 ? 2 * (row & 7) : 2 * (row & 3);
 }
+__device__ __forceinline__ int swz_vt(int d) { return (d >> 1) & 7; }
 
 // One 16-byte-per-lane direct load from global memory into LDS: lane l's 16 bytes land at
 // lds + 16 l (global_load_lds_dwordx4).  The builtin only exists for the device; the host
@@ -79,8 +103,25 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ i16x4 tr_read_b64(const unsigned char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)(p);
+}
+
+// Four transposing 64-bit LDS reads (ds_read_b64_tr_b16), completed before the block ends.
+// Written as one asm block with its own wait: the compiler treats the builtin as a possible
+// reader of the direct-load destinations and would otherwise drain every outstanding direct
+// load (vmcnt(0)) in front of it, which stalls the tile prefetch each iteration.  Callers
+// order these reads after the data landed (wait_and_barrier).
+__device__ __forceinline__ void tr_read_b64_x4(const unsigned char* const (&p)[4], i16x4 (&r)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(lds_addr(p[0])), "v"(lds_addr(p[1])), "v"(lds_addr(p[2])), "v"(lds_addr(p[3]))
+      : "memory");
 }
 
 __device__ __forceinline__ _Float16 bf16_bits_to_f16(short h) {
@@ -102,8 +143,8 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 // Wait until at most N of this wave's vector-memory operations are outstanding (the LDS
-// direct loads of later tiles), then barrier.  The LDS reads issued before are drained
-// too, so a stage may be refilled right after the barrier.
+// direct loads of later tiles), then barrier.  The LDS accesses issued before are drained
+// too, so a buffer may be refilled right after the barrier.
 template <int N>
 __device__ __forceinline__ void wait_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
@@ -118,18 +159,22 @@ struct PrefixArgs {
   float* o_part;
   Geometry g;
   int32_t row_blocks;              // query-row blocks per (b, kv head)
-  int32_t tiles_per_block;         // row tiles per block (MT * 4 + leftover)
-  int32_t leftover;                // tiles_per_block - 4 * MT, 0..3
+  int32_t tiles_per_block;         // row tiles per block
   float c;                         // scale * log2(e)
 };
 
+// MT full row tiles per wave (both wave groups); NL leftover tiles (0..2) per block, split
+// over the second wave group by output d-blocks.
 template <int D, int MT, int NL>
 __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) {
   using Y = Layout<D>;
   constexpr int DS = D / 32;  // 32-wide d steps of the score product
   constexpr int DB = D / 16;  // 16-wide d blocks of the output
   constexpr int DPW = Y::kDmaPerWave;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[kStages * Y::kStageBytes];
+  constexpr int P = 2 * DPW;  // direct loads per first-group wave per tile (K and V)
+  constexpr int MTA = MT > 0 ? MT : 1;
+  constexpr bool LEFT = NL > 0;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[Y::kBytes];
 
   const Geometry& G = a.g;
   const int s = blockIdx.x;
@@ -137,7 +182,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   const int rb = blockIdx.y % a.row_blocks;
   const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform by construction; readfirstlane lets the compiler see it (scalar branches)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wg = wave >> 2;  // wave group (one wave of each group per SIMD)
+  const int ww = wave & 3;   // wave within its group
   const int l16 = lane & 15;
   const int grp = lane >> 4;
 
@@ -152,22 +200,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   const unsigned short* Kg = a.k_prefix + kv_base;
   const unsigned short* Vg = a.v_prefix + kv_base;
 
-  // ---- stream K/V tiles into the LDS ring
-  auto issue = [&](int t) {
-    unsigned char* st = lds + (t % kStages) * Y::kStageBytes;
-    const int key0 = kbeg + t * kKeyTile;
-#pragma unroll
-    for (int j = 0; j < DPW; ++j) {
-      const int blk = j * kWaves + wave;  // 1 KB block of the tile written by this wave
-      const int u = 64 * blk + lane;      // 16-byte chunk position within the tile
-      const int r = u / Y::kChunks, p = u % Y::kChunks;
-      const size_t gk = (size_t)min(key0 + r, kend - 1);
-      lds_dma16(Kg + gk * D + 8 * (p ^ swz_k<D>(r)), st + 1024 * blk);
-      lds_dma16(Vg + gk * D + 8 * (p ^ swz_v<D>(r)), st + Y::kTileBytes + 1024 * blk);
-    }
-  };
-
-  // ---- row tiles of this wave; query operand (B of S^T): Q[row = l16][d = 32 ds + 8 grp ..]
+  // ---- query operands (B of S^T): Q[row = l16][d = 32 ds + 8 grp ..], kept in registers
   const int t0 = rb * a.tiles_per_block;
   const int t_end = min(t0 + a.tiles_per_block, G.NT);
   auto load_q = [&](int tile, bf16x8* dst) {
@@ -180,195 +213,337 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     for (int ds = 0; ds < DS; ++ds)
       dst[ds] = as_bf16x8(ok ? *(const uint4*)(qp + 32 * ds) : make_uint4(0, 0, 0, 0));
   };
-  constexpr int MTA = MT > 0 ? MT : 1;
+  auto full_tile = [&](int k) { return t0 + wg * (kWaves / 2) * MT + 4 * k + ww; };
   bf16x8 qop[MTA][DS];
-#pragma unroll
-  for (int k = 0; k < MT; ++k) load_q(t0 + kWaves * k + wave, qop[k]);
-  // The query operands live in AGPRs for the whole kernel (MFMA reads its B operand from
-  // AGPRs), leaving the VGPR file to scores, probabilities and operand staging.
-#pragma unroll
-  for (int k = 0; k < MT; ++k)
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) asm volatile("" : "+a"(qop[k][ds]));
 
-  // Leftover tile (NL = 1 or 2 of them): shared by 4/NL waves; each computes its scores in
-  // full but only LDB of the DB output d-blocks, starting at ldb0.
-  constexpr int LDB = NL > 0 ? DB * NL / kWaves : 1;
-  const int ltile = t0 + kWaves * MT + (NL == 2 ? (wave >> 1) : 0);
-  const int ldb0 = NL > 0 ? (wave % (kWaves / (NL > 0 ? NL : 1))) * LDB : 0;
+  // Leftover tiles (second wave group only): NL = 1 -> one tile shared by its 4 waves,
+  // NL = 2 -> tile ww/2 shared by 2 waves; each wave owns LDB output d-blocks from ldb0.
+  constexpr int LDB = NL > 0 ? DB * NL / 4 : 1;
+  const bool has_left = LEFT && wg == 1;
+  const int ltile = t0 + kWaves * MT + (NL == 2 ? (ww >> 1) : 0);
+  const int ldb0 = (NL == 2 ? (ww & 1) : ww) * LDB;
   bf16x8 qopl[DS];
-  if (NL > 0) {
-    load_q(ltile, qopl);
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) asm volatile("" : "+a"(qopl[ds]));
-  }
 
-  const int npre = min(kStages - 1, ntiles);
-  for (int t = 0; t < npre; ++t) issue(t);
+  // ---- stream K/V tiles into the LDS rings
+  auto issue = [&](int t) {
+    unsigned char* ks = lds + Y::kKRing + (t % kKStages) * Y::kTileBytes;
+    unsigned char* vs = lds + Y::kVRing + (t % kVStages) * Y::kTileBytes;
+    const int key0 = kbeg + t * kKeyTile;
+#pragma unroll
+    for (int j = 0; j < DPW; ++j) {
+      const int blk = j * 4 + ww;         // 1 KB block of the tile written by this wave
+      const int u = 64 * blk + lane;      // 16-byte chunk position within the tile
+      const int r = u / Y::kChunks, p = u % Y::kChunks;
+      const size_t gk = (size_t)min(key0 + r, kend - 1);
+      lds_dma16(Kg + gk * D + 8 * (p ^ swz_k<D>(r)), ks + 1024 * blk);
+      lds_dma16(Vg + gk * D + 8 * (p ^ swz_v<D>(r)), vs + 1024 * blk);
+    }
+  };
+
+  // ---- V (bf16, keys x d) -> V^T (fp16, d x keys in P^T operand order).  Lane (grp, l16)
+  // of (d block db, 32-key half ks) produces d = 16 db + l16, keys 32 ks + 16 (e/4) +
+  // 4 grp + e%4 for e = 0..7: one 16-byte chunk, position 4 ks + grp of row d.
+  const int vr = lane & 15;
+  const int vrow = 4 * grp + (vr >> 2);
+  const int vch = (vr & 3) >> 1, vhalf = 8 * (vr & 1);
+  auto transpose_v = [&](int t) {
+    const unsigned char* vs = lds + Y::kVRing + (t % kVStages) * Y::kTileBytes;
+    unsigned char* vt = lds + Y::kVt + (t % kVtStages) * Y::kTileBytes;
+    constexpr int kUnits = 2 * DB / 4;  // (d block, half) units per first-group wave
+    static_assert(kUnits % 2 == 0, "units are read in pairs");
+#pragma unroll
+    for (int i = 0; i < kUnits; i += 2) {
+      const unsigned char* src[4];
+      int dst[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int pr = ww + 4 * (i + u);
+        const int db = pr >> 1, ks = pr & 1;
+        const int r0 = 32 * ks + vrow, r1 = r0 + 16;
+        const int c = 2 * db + vch;
+        src[2 * u] = vs + r0 * Y::kRowBytes + 16 * (c ^ swz_v<D>(r0)) + vhalf;
+        src[2 * u + 1] = vs + r1 * Y::kRowBytes + 16 * (c ^ swz_v<D>(r1)) + vhalf;
+        const int d = 16 * db + l16;
+        dst[u] = d * (kKeyTile * 2) + 16 * ((4 * ks + grp) ^ swz_vt(d));
+      }
+      i16x4 r[4];
+      tr_read_b64_x4(src, r);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        f16x8 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          h[e] = bf16_bits_to_f16(r[2 * u][e]);
+          h[4 + e] = bf16_bits_to_f16(r[2 * u + 1][e]);
+        }
+        *(f16x8*)(vt + dst[u]) = h;
+      }
+    }
+  };
+
+  // barrier once at most `n` tiles of this wave's direct loads are still outstanding
+  // (only first-group waves have direct loads in flight; the others just meet the barrier)
+  auto wait_tiles_and_barrier = [&](int n) {
+    if (wg != 0) wait_and_barrier<0>();
+    else if (n >= 2) wait_and_barrier<2 * P>();
+    else if (n == 1) wait_and_barrier<P>();
+    else wait_and_barrier<0>();
+  };
 
   f32x4 acc[MTA][DB];
   f32x4 accl[LDB];
-  float m_run[MTA], l_run[MTA], m_l = -INFINITY, l_l = 0.f;
+  float l_run[MTA], l_l = 0.f;
 #pragma unroll
   for (int k = 0; k < MT; ++k) {
-    m_run[k] = -INFINITY;
     l_run[k] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[k][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int j = 0; j < LDB; ++j) accl[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int vr = lane & 15;  // lane within its 16-lane block, for the transposing reads
-  const int vrow = 4 * grp + (vr >> 2);
-  const int vch = (vr & 3) >> 1, vhalf = 8 * (vr & 1);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int after = min(kStages - 2, ntiles - 1 - t);  // tiles issued after t
-    if (after >= 2) wait_and_barrier<4 * DPW>();
-    else if (after == 1) wait_and_barrier<2 * DPW>();
-    else wait_and_barrier<0>();
-    if (t + kStages - 1 < ntiles) issue(t + kStages - 1);  // refills the stage of tile t-1
+  // P^T operands of the half in flight: made by the softmax step, consumed by the PV step
+  f16x8 pop[MTA];
+  f16x8 popl;
+  // Softmax reference per row (log2 units): starts at the maximum of the chunk's first 32
+  // keys and is only raised when a lane's 8 probabilities of a half sum above kRaiseP, so
+  // p = 2^(s c - m_ref) < 2^8 always fits fp16 and the accumulator rescale is rare.
+  float m_ref[MTA], m_refl = 0.f;
 
-    const unsigned char* Ks = lds + (t % kStages) * Y::kStageBytes;
-    const unsigned char* Vs = Ks + Y::kTileBytes;
+  // ---- scores S^T[key][row] of keys 32 h .. 32 h + 31 of tile t: this lane holds row l16,
+  // keys 32 h + 16 j + 4 grp + r in sc[.][j][r]; keys past the chunk end get -inf
+  auto scores = [&](auto tag, int t, int h, f32x4 (&sc)[MTA][2], f32x4 (&scl)[2]) {
+    constexpr bool WL = decltype(tag)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    const unsigned char* Ks = lds + Y::kKRing + (t % kKStages) * Y::kTileBytes;
     const int key0 = kbeg + t * kKeyTile;
-    const bool partial = key0 + kKeyTile > kend;
-
-    // Two halves of 32 keys: half h covers key blocks 2h, 2h+1 (scores) and feeds the PV
-    // product's k-step h.
+    // all K operands of the half are read up front, so the products start as soon as the
+    // first ones land and the rest of the reads overlap them
+    bf16x8 kop[DS][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // ---- scores S^T[key][row]: this lane holds row l16, keys 32 h + 16 j + 4 grp + r
-      f32x4 sc[MTA][2];
-      f32x4 scl[2];
+    for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int row = 32 * h + 16 * j + l16;
-          const bf16x8 kop = *(const bf16x8*)(Ks + row * Y::kRowBytes +
-                                              16 * ((4 * ds + grp) ^ swz_k<D>(row)));
-#pragma unroll
-          for (int k = 0; k < MT; ++k)
-            sc[k][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[k][ds],
-                                                               ds ? sc[k][j] : zero4, 0, 0, 0);
-          if (NL > 0)
-            scl[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qopl[ds], ds ? scl[j] : zero4,
-                                                             0, 0, 0);
-        }
+      for (int j = 0; j < 2; ++j) {
+        const int row = 32 * h + 16 * j + l16;
+        kop[ds][j] = *(const bf16x8*)(Ks + row * Y::kRowBytes + 16 * ((4 * ds + grp) ^ swz_k<D>(row)));
       }
-
-      // ---- keys past the chunk end (last tile only)
-      if (partial) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+    for (int ds = 0; ds < DS; ++ds) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (key0 + 32 * h + 16 * j + 4 * grp + r >= kend) {
-#pragma unroll
-              for (int k = 0; k < MT; ++k) sc[k][j][r] = -INFINITY;
-              if (NL > 0) scl[j][r] = -INFINITY;
-            }
-      }
-
-      // ---- online softmax with a lazily raised reference maximum
-      float lmax[MTA], lmaxl = -INFINITY;
-      bool need = false;
-#pragma unroll
-      for (int k = 0; k < MT; ++k) {
-        const float m0 = fmaxf(fmaxf(sc[k][0][0], sc[k][0][1]), fmaxf(sc[k][0][2], sc[k][0][3]));
-        const float m1 = fmaxf(fmaxf(sc[k][1][0], sc[k][1][1]), fmaxf(sc[k][1][2], sc[k][1][3]));
-        lmax[k] = fmaxf(m0, m1) * a.c;
-        need |= lmax[k] > m_run[k] + kRescaleSlack;
-      }
-      if (NL > 0) {
-        const float m0 = fmaxf(fmaxf(scl[0][0], scl[0][1]), fmaxf(scl[0][2], scl[0][3]));
-        const float m1 = fmaxf(fmaxf(scl[1][0], scl[1][1]), fmaxf(scl[1][2], scl[1][3]));
-        lmaxl = fmaxf(m0, m1) * a.c;
-        need |= lmaxl > m_l + kRescaleSlack;
-      }
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-        for (int k = 0; k < MT; ++k) {
-          const float m_new = fmaxf(m_run[k], group_max(lmax[k]));
-          const float alpha = __builtin_amdgcn_exp2f(m_run[k] - m_new);
-          m_run[k] = m_new;
-          l_run[k] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) acc[k][db] *= alpha;
-        }
-        if (NL > 0) {
-          const float m_new = fmaxf(m_l, group_max(lmaxl));
-          const float alpha = __builtin_amdgcn_exp2f(m_l - m_new);
-          m_l = m_new;
-          l_l *= alpha;
-#pragma unroll
-          for (int j = 0; j < LDB; ++j) accl[j] *= alpha;
-        }
-      }
-
-      // P^T operand of k-step h: element e <-> key 32 h + 16 (e / 4) + 4 grp + (e % 4)
-      f16x8 pop[MTA];
-      f16x8 popl;
-#pragma unroll
-      for (int k = 0; k < MT; ++k) {
-        float ls = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[k][e / 4][e % 4], a.c, -m_run[k]));
-          ls += p;
-          pop[k][e] = (_Float16)p;
-        }
-        l_run[k] += ls;
-      }
-      if (NL > 0) {
-        float ls = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(scl[e / 4][e % 4], a.c, -m_l));
-          ls += p;
-          popl[e] = (_Float16)p;
-        }
-        l_l += ls;
-      }
-
-      // ---- O^T[d][row] += V^T[d][key] P^T[key][row]  (keys 32 h .. 32 h + 31)
-      auto v_operand = [&](int db) {
-        const int r0 = 32 * h + vrow, r1 = r0 + 16;
-        const int c = 2 * db + vch;
-        const i16x4 lo = tr_read_b64(Vs + r0 * Y::kRowBytes + 16 * (c ^ swz_v<D>(r0)) + vhalf);
-        const i16x4 hi = tr_read_b64(Vs + r1 * Y::kRowBytes + 16 * (c ^ swz_v<D>(r1)) + vhalf);
-        f16x8 vop;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vop[e] = bf16_bits_to_f16(lo[e]);
-          vop[4 + e] = bf16_bits_to_f16(hi[e]);
-        }
-        return vop;
-      };
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f16x8 vop = v_operand(db);
+      for (int j = 0; j < 2; ++j) {
 #pragma unroll
         for (int k = 0; k < MT; ++k)
-          acc[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[k], acc[k][db], 0, 0, 0);
-      }
-      if (NL > 0) {
-#pragma unroll
-        for (int j = 0; j < LDB; ++j)
-          accl[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v_operand(ldb0 + j), popl, accl[j], 0,
-                                                           0, 0);
+          sc[k][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ds][j], qop[k][ds],
+                                                             ds ? sc[k][j] : zero4, 0, 0, 0);
+        if constexpr (WL)
+          scl[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ds][j], qopl[ds], ds ? scl[j] : zero4,
+                                                           0, 0, 0);
       }
     }
-  }
+    // instruction order: operand reads run two d-steps ahead of the products
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * (MT + (WL ? 1 : 0)), 0);
+      if (ds + 2 < DS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (key0 + 32 * h + 32 > kend) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (key0 + 32 * h + 16 * j + 4 * grp + r >= kend) {
+#pragma unroll
+            for (int k = 0; k < MT; ++k) sc[k][j][r] = -INFINITY;
+            if constexpr (WL) scl[j][r] = -INFINITY;
+          }
+    }
+  };
+
+  // ---- reference of the pass: maximum of the chunk's first 32 keys (tile 0 in LDS; it
+  // always holds a valid key)
+  auto set_reference = [&](auto tag) {
+    constexpr bool WL = decltype(tag)::value;
+    f32x4 sc[MTA][2];
+    f32x4 scl[2];
+    scores(tag, 0, 0, sc, scl);
+#pragma unroll
+    for (int k = 0; k < MT; ++k) {
+      const float m0 = fmaxf(fmaxf(sc[k][0][0], sc[k][0][1]), fmaxf(sc[k][0][2], sc[k][0][3]));
+      const float m1 = fmaxf(fmaxf(sc[k][1][0], sc[k][1][1]), fmaxf(sc[k][1][2], sc[k][1][3]));
+      m_ref[k] = group_max(fmaxf(m0, m1) * a.c);
+    }
+    if constexpr (WL) {
+      const float m0 = fmaxf(fmaxf(scl[0][0], scl[0][1]), fmaxf(scl[0][2], scl[0][3]));
+      const float m1 = fmaxf(fmaxf(scl[1][0], scl[1][1]), fmaxf(scl[1][2], scl[1][3]));
+      m_refl = group_max(fmaxf(m0, m1) * a.c);
+    }
+  };
+
+  // ---- step X(t, h): scores of keys 32 h .. 32 h + 31 of tile t, softmax, P^T operands
+  auto qk_softmax = [&](auto tag, int t, int h) {
+    constexpr bool WL = decltype(tag)::value;
+    f32x4 sc[MTA][2];
+    f32x4 scl[2];
+    scores(tag, t, h, sc, scl);
+    // ---- probabilities against the running reference (fp32)
+    float p[MTA][8], pl[8], ls[MTA], lsl = 0.f;
+#pragma unroll
+    for (int k = 0; k < MT; ++k) {
+      ls[k] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[k][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[k][e / 4][e % 4], a.c, -m_ref[k]));
+        ls[k] += p[k][e];
+      }
+    }
+    if constexpr (WL) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pl[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(scl[e / 4][e % 4], a.c, -m_refl));
+        lsl += pl[e];
+      }
+    }
+    // ---- raise the reference of rows whose probabilities outgrew kRaiseP (rare: the
+    // reference starts at the maximum of the chunk's first 32 keys); wave-uniform branch
+    bool need = false;
+#pragma unroll
+    for (int k = 0; k < MT; ++k) need |= ls[k] > kRaiseP;
+    if constexpr (WL) need |= lsl > kRaiseP;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+      for (int k = 0; k < MT; ++k) {
+        const float mx = group_max(ls[k]);
+        // mx bounds the row's largest probability from above: the new reference is at least
+        // the row's largest score so far, so every probability drops to at most 1
+        const float shift = mx > kRaiseP ? __log2f(mx) : 0.f;
+        const float alpha = __builtin_amdgcn_exp2f(-shift);
+        m_ref[k] += shift;
+        l_run[k] *= alpha;
+        ls[k] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[k][e] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[k][db] *= alpha;
+      }
+      if constexpr (WL) {
+        const float mx = group_max(lsl);
+        const float shift = mx > kRaiseP ? __log2f(mx) : 0.f;
+        const float alpha = __builtin_amdgcn_exp2f(-shift);
+        m_refl += shift;
+        l_l *= alpha;
+        lsl *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pl[e] *= alpha;
+#pragma unroll
+        for (int j = 0; j < LDB; ++j) accl[j] *= alpha;
+      }
+    }
+    // P^T operand of k-step h: element e <-> key 32 h + 16 (e / 4) + 4 grp + (e % 4)
+#pragma unroll
+    for (int k = 0; k < MT; ++k) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pop[k][e] = (_Float16)p[k][e];
+      l_run[k] += ls[k];
+    }
+    if constexpr (WL) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) popl[e] = (_Float16)pl[e];
+      l_l += lsl;
+    }
+  };
+
+  // ---- step Y(t, h): O^T[d][row] += V^T[d][key] P^T[key][row] for keys 32 h .. 32 h + 31
+  auto pv = [&](auto tag, int t, int h) {
+    constexpr bool WL = decltype(tag)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    const unsigned char* Vt = lds + Y::kVt + (t % kVtStages) * Y::kTileBytes;
+    f16x8 vop[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d = 16 * db + l16;
+      vop[db] = *(const f16x8*)(Vt + d * (kKeyTile * 2) + 16 * ((4 * h + grp) ^ swz_vt(d)));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int k = 0; k < MT; ++k)
+        acc[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[db], pop[k], acc[k][db], 0, 0, 0);
+    // instruction order: operand reads run four d-blocks ahead of the products
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, MT, 1);
+      if (db + 4 < DB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 1);
+    }
+    if constexpr (WL) {
+      // ldb0 is a runtime value: re-read these operands rather than index a register array
+      // with it (that would put the array in scratch memory)
+#pragma unroll
+      for (int j = 0; j < LDB; ++j) {
+        const int d = 16 * (ldb0 + j) + l16;
+        const f16x8 vl =
+            *(const f16x8*)(Vt + d * (kKeyTile * 2) + 16 * ((4 * h + grp) ^ swz_vt(d)));
+        accl[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, popl, accl[j], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- pass over the chunk.  Tiles stream through the LDS rings: tile t+3 is issued while
+  // tile t is consumed and V of tile t+1 is transposed.  Each wave works through the 32-key
+  // halves as X(t,0) Y(t,0) X(t,1) Y(t,1) (X: scores and softmax, Y: PV); the second wave
+  // group runs one step behind the first (it finishes Y(t-1,1) at the start of tile t), so on
+  // each SIMD one wave's softmax arithmetic overlaps the other's matrix products.  Only the
+  // second group carries leftover rows.
+  auto run_chunk = [&](auto group) {
+    constexpr bool LAG = decltype(group)::value;  // second wave group
+    constexpr std::integral_constant<bool, LAG && LEFT> tag{};
+    if constexpr (!LAG)
+      for (int t = 0; t < 3 && t < ntiles; ++t) issue(t);
+    // the query loads queue behind the first tiles (the compiler drains every vector-memory
+    // load before the first use of their registers, so issuing them first would serialise
+    // their latency with that of the tiles)
+#pragma unroll
+    for (int k = 0; k < MT; ++k) load_q(full_tile(k), qop[k]);
+    if constexpr (decltype(tag)::value) load_q(ltile, qopl);
+    wait_tiles_and_barrier(min(2, ntiles - 1));
+    set_reference(tag);
+    if constexpr (!LAG) transpose_v(0);
+    for (int t = 0; t < ntiles; ++t) {
+      // tile t+1 landed (for the transpose), V^T of tile t complete, tile t-1 done
+      wait_tiles_and_barrier(min(t + 2, ntiles - 1) - (t + 1));
+      if constexpr (!LAG) {
+        if (t + 3 < ntiles) issue(t + 3);  // refills the K stage of t-1 and the V stage of t
+        if (t + 1 < ntiles) transpose_v(t + 1);
+      }
+      if constexpr (!LAG) {
+        qk_softmax(tag, t, 0);
+        pv(tag, t, 0);
+        qk_softmax(tag, t, 1);
+        pv(tag, t, 1);
+      } else {
+        if (t > 0) pv(tag, t - 1, 1);
+        qk_softmax(tag, t, 0);
+        pv(tag, t, 0);
+        qk_softmax(tag, t, 1);
+      }
+    }
+    if constexpr (LAG) pv(tag, ntiles - 1, 1);
+  };
+
+  // the two groups run separate copies of the loop (same barrier sequence), so each copy
+  // is register-allocated on its own
+  if (wg == 0) run_chunk(std::false_type{});
+  else run_chunk(std::true_type{});
 
   // ---- normalise and write this chunk's partial
   const size_t slot = ((size_t)b * G.Hkv + kv) * (G.S + 1) + s;
 #pragma unroll
   for (int k = 0; k < MT; ++k) {
-    const int tile = t0 + kWaves * k + wave;
+    const int tile = full_tile(k);
     const float lt = group_sum(l_run[k]);
     if (tile >= t_end) continue;
     const int row = tile * 16 + l16;
@@ -376,17 +551,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     float* op = a.o_part + (slot * G.R_pad + row) * D + 4 * grp;
 #pragma unroll
     for (int db = 0; db < DB; ++db) *(f32x4*)(op + 16 * db) = acc[k][db] * inv;
-    if (grp == 0) a.lse_part[slot * G.R_pad + row] = (m_run[k] + __log2f(lt)) * kLn2;
+    if (grp == 0) a.lse_part[slot * G.R_pad + row] = (m_ref[k] + __log2f(lt)) * kLn2;
   }
-  if (NL > 0) {
+  if (LEFT) {
+    // every sharer of a leftover tile holds the same m_l and l_l; each writes its d-blocks
     const float lt = group_sum(l_l);
-    if (ltile < t_end) {
+    if (has_left && ltile < t_end) {
       const int row = ltile * 16 + l16;
       const float inv = 1.f / lt;
       float* op = a.o_part + (slot * G.R_pad + row) * D + 4 * grp;
 #pragma unroll
       for (int j = 0; j < LDB; ++j) *(f32x4*)(op + 16 * (ldb0 + j)) = accl[j] * inv;
-      if (grp == 0 && ldb0 == 0) a.lse_part[slot * G.R_pad + row] = (m_l + __log2f(lt)) * kLn2;
+      if (grp == 0 && ldb0 == 0) a.lse_part[slot * G.R_pad + row] = (m_refl + __log2f(lt)) * kLn2;
     }
   }
 }
@@ -398,8 +574,8 @@ hipError_t launch_cfg(const PrefixArgs& a, dim3 grid, hipStream_t stream) {
 }
 
 template <int D, int MT>
-hipError_t launch_mt(const PrefixArgs& a, dim3 grid, hipStream_t stream) {
-  switch (a.leftover) {
+hipError_t launch_mt(const PrefixArgs& a, int nl, dim3 grid, hipStream_t stream) {
+  switch (nl) {
     case 0: return launch_cfg<D, MT, 0>(a, grid, stream);
     case 1: return launch_cfg<D, MT, 1>(a, grid, stream);
     case 2: return launch_cfg<D, MT, 2>(a, grid, stream);
@@ -408,31 +584,40 @@ hipError_t launch_mt(const PrefixArgs& a, dim3 grid, hipStream_t stream) {
 }
 
 template <int D>
-hipError_t launch_d(const PrefixArgs& a, int mt, dim3 grid, hipStream_t stream) {
+hipError_t launch_d(const PrefixArgs& a, int mt, int nl, dim3 grid, hipStream_t stream) {
   switch (mt) {
-    case 0: return launch_mt<D, 0>(a, grid, stream);
-    case 1: return launch_mt<D, 1>(a, grid, stream);
-    case 2: return launch_mt<D, 2>(a, grid, stream);
-    case 3: return launch_mt<D, 3>(a, grid, stream);
-    case 4: return launch_mt<D, 4>(a, grid, stream);
-    case 5: return launch_mt<D, 5>(a, grid, stream);
+    case 0: return launch_mt<D, 0>(a, nl, grid, stream);
+    case 1: return launch_mt<D, 1>(a, nl, grid, stream);
+    case 2: return launch_mt<D, 2>(a, nl, grid, stream);
     default: return hipErrorInvalidValue;
+  }
+}
+
+// Tiles per workgroup: 8 * mt full tiles plus nl leftover tiles.  The register budget of
+// two waves per SIMD (256 VGPRs, no scratch) admits (mt, nl) in {(0..1, 0..2), (2, 0..1)}:
+// at most 17 tiles (272 query rows) per workgroup; more rows are split into row blocks.
+// Any other tile count rounds up to 8 * mt slots (the surplus slots compute nothing useful).
+void split_rows(int tiles, int* mt, int* nl) {
+  const int m = tiles / 8, r = tiles % 8;
+  if (r == 0 || (r == 1 && m <= 2) || (r == 2 && m <= 1)) {
+    *mt = m;
+    *nl = r;
+  } else {
+    *mt = (tiles + 7) / 8;
+    *nl = 0;
   }
 }
 
 }  // namespace
 
-// Row blocking: a workgroup covers up to 18 row tiles (288 query rows): 4 full tiles per
-// wave plus up to two shared leftover tiles.  A remainder of three tiles becomes one more
-// full slot per wave (the fourth wave's slot is empty).  More rows are split into equal
-// row blocks.
 void prefix_row_blocking(const Geometry& g, int* mt, int* tiles_per_block, int* blocks) {
-  const int max_tiles = 4 * 4 + 2;
+  const int max_tiles = 8 * 2 + 1;
   const int nb = (g.NT + max_tiles - 1) / max_tiles;
   const int tpb = (g.NT + nb - 1) / nb;
+  int nl;
+  split_rows(tpb, mt, &nl);
   *blocks = (g.NT + tpb - 1) / tpb;
   *tiles_per_block = tpb;
-  *mt = tpb % 4 == 3 ? tpb / 4 + 1 : tpb / 4;
 }
 
 hipError_t launch_prefix_attn_splitk(const Geometry& g, const void* q, const void* k_prefix,
@@ -446,15 +631,15 @@ hipError_t launch_prefix_attn_splitk(const Geometry& g, const void* q, const voi
   a.lse_part = ws.lse_part;
   a.o_part = ws.o_part;
   a.g = g;
-  int mt, tpb, nb;
+  int mt, tpb, nb, nl;
   prefix_row_blocking(g, &mt, &tpb, &nb);
+  split_rows(tpb, &mt, &nl);
   a.row_blocks = nb;
   a.tiles_per_block = tpb;
-  a.leftover = tpb % 4 == 3 ? 0 : tpb - 4 * mt;
   a.c = g.scale * kLog2e;
   dim3 grid(g.S, g.Hkv * nb, g.B);
-  if (g.D == 128) return launch_d<128>(a, mt, grid, stream);
-  if (g.D == 64) return launch_d<64>(a, mt, grid, stream);
+  if (g.D == 128) return launch_d<128>(a, mt, nl, grid, stream);
+  if (g.D == 64) return launch_d<64>(a, mt, nl, grid, stream);
   return hipErrorInvalidValue;
 }
 
