@@ -150,11 +150,11 @@ hta_status hta_verify(const hta_desc* desc, const void* q, const void* k_prefix,
   HTA_TRY(check_ws(p, workspace, workspace_bytes));
   const Workspace ws = carve(workspace, p);
   hipStream_t s = (hipStream_t)stream;
-  HTA_TRY(hip_status(hta::launch_tree_attn_masked(G, q, k_tree, v_tree, parent_idx, prefix_len,
-                                                  ws, ws.masks, true, s)));
+  // two launches: the split-K prefix pass, then the merge with the tree part fused in
   HTA_TRY(hip_status(
       hta::launch_prefix_attn_splitk(G, q, k_prefix, v_prefix, prefix_len, ws, s)));
-  return hip_status(hta::launch_lse_merge(G, prefix_len, true, out, lse, ws, s));
+  return hip_status(hta::launch_tree_merge(G, q, k_tree, v_tree, parent_idx, prefix_len, out,
+                                           lse, ws, s));
 }
 
 hta_status hta_ancestor_masks(const hta_desc* desc, const int32_t* parent_idx, uint64_t* masks,

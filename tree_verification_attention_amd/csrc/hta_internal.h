@@ -53,6 +53,12 @@ hipError_t launch_tree_attn_masked(const Geometry& g, const void* q, const void*
                                    uint64_t* masks_out, bool attention, hipStream_t stream);
 hipError_t launch_lse_merge(const Geometry& g, const int32_t* prefix_len, bool include_tree,
                             float* out, float* lse, const Workspace& ws, hipStream_t stream);
+// The merge with the tree part computed in the same kernel (validates the trees and writes
+// the device status): the second half of the whole step after the prefix pass.
+hipError_t launch_tree_merge(const Geometry& g, const void* q, const void* k_tree,
+                             const void* v_tree, const int32_t* parent_idx,
+                             const int32_t* prefix_len, float* out, float* lse,
+                             const Workspace& ws, hipStream_t stream);
 
 // How the prefix pass blocks the query rows of one KV head: mt full row tiles per wave,
 // tiles_per_block row tiles per workgroup, blocks workgroups per (sequence, KV head, chunk).

@@ -1,18 +1,34 @@
 // lse_merge.hip -- the aggregation step of tree verification attention on gfx950.
 //
-// The prefix pass and the tree pass each produce a normalised partial attention and its
-// log-sum-exp over a disjoint set of keys; LongSpec aggregates them into the attention over
-// the union (README, Introduction, "Hybrid Attention Aggregation"; arXiv abstract).  Since
-// the decoding is lossless the aggregation must be exact, which the log-sum-exp merge is:
-//     M = max_s lse_s,   w_s = exp(lse_s - M),
-//     out = sum_s w_s o_s / sum_s w_s,   lse = M + ln sum_s w_s.
+// The prefix pass and the tree pass each produce a partial attention and its log-sum-exp
+// over a disjoint set of keys; LongSpec aggregates them into the attention over the union
+// (README, Introduction, "Hybrid Attention Aggregation"; arXiv abstract).  Since the
+// decoding is lossless the aggregation must be exact, which the log-sum-exp merge is (in
+// log2 units, L_s = lse_s * log2(e)):
+//     M = max_s L_s,   w_s = 2^(L_s - M),
+//     out = sum_s w_s o_s / sum_s w_s,   lse = (M + log2 sum_s w_s) * ln(2).
 // Here the parts are the split-K chunks of the prefix (only the ceil(prefix_len/chunk)
-// non-empty ones are read) and the tree partial.
+// non-empty ones are read) and the tree part.
 //
-// One wave per output row (b, i, h): lane s reads lse of part s, the wave reduces the
-// maximum and the weight sum, then the lanes own output dimensions (D/64 each) and stream
-// the partial rows with coalesced loads.  Output rows are contiguous in out [B, T, Hq, D],
-// so consecutive waves write consecutive 512-byte rows.
+// One wave per output row (b, i, h), in four part groups of 16 lanes: group g handles prefix
+// splits g, g+4, g+8, ... and each of its lanes owns D/16 consecutive output dimensions
+// (16- or 32-byte loads), so a group reads whole 512-byte partial rows.  Every load of the
+// first 36 splits (their log-sum-exps and partial rows), the tree part and the sequence's
+// prefix length is issued before any is used, so the merge costs one memory round trip: the
+// slots of splits past the prefix end are read speculatively and never used (they
+// contribute through a select, never a multiply by zero, so stale contents are harmless).
+// The four group sums are added across lanes l, l^16, l^32, l^48 and the first group writes
+// the row.
+//
+// Two forms.  The plain merge reads the tree partial (slot S) written by tree_attn_masked.
+// The fused merge, used by the whole step, computes the tree part itself: a query row sees
+// exactly its node's ancestors and itself, at most depth + 1 keys, so the wave walks the
+// parent chain (the sequence's parent pointers staged in LDS and validated as they load)
+// and takes the visible keys four at a time, one per part group: each group forms its key's
+// score with a 16-lane reduction over D, and the groups keep a running maximum, weight sum
+// and weighted value sum in fp32.  This replaces a launch and the partial round trip
+// through HBM with a few dozen dot products per row.  The fused merge also records the
+// sequence's device status.
 #include "hta_internal.h"
 
 namespace hta {
@@ -21,13 +37,21 @@ namespace {
 
 constexpr int kThreads = 256;
 
+constexpr int kMaxT = 256;
+
 struct MergeArgs {
   const int32_t* prefix_len;
-  const int32_t* status;   // [B] or null
+  const int32_t* status;   // [B] or null: read by the plain merge
   const float* lse_part;
   const float* o_part;
   float* out;
   float* lse;
+  // fused merge only
+  const unsigned short* q;       // bf16 [B, T, Hq, D]
+  const unsigned short* k_tree;  // [B, Hkv, T, D]
+  const unsigned short* v_tree;
+  const int32_t* parent_idx;     // [B, T]
+  int32_t* status_out;           // [B]
   Geometry g;
   int32_t include_tree;
 };
@@ -38,18 +62,44 @@ __device__ inline float wave_max(float x) {
   return x;
 }
 
-__device__ inline float wave_sum(float x) {
+// sum over the four part groups (lanes l, l^16, l^32, l^48)
+__device__ inline float group_sum4(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ inline float bf16_to_f32(unsigned short h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+// sum over the 16 lanes of a part group
+__device__ inline float lane16_sum(float x) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o);
   return x;
 }
 
-template <int D>
+// maximum over the four part groups (lanes l, l^16, l^32, l^48)
+__device__ inline float group_max4(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+template <int D, bool FUSED>
 __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
-  constexpr int DPL = D / 64;
+  constexpr int DPL = D / 16;   // output dimensions per lane of a part group
+  constexpr int NV = DPL / 4;   // float4 loads per part and lane
+  constexpr int kBatch = 9;     // splits per lane per pass: 36 per pass
+  __shared__ int32_t s_par[kThreads / 64][kMaxT];  // fused: parent pointers, one slice per wave
   const Geometry& G = a.g;
   const int lane = threadIdx.x & 63;
-  const long row_id = (long)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int pg = lane >> 4, dl = lane & 15;
+  const long row_id = (long)blockIdx.x * (kThreads / 64) + wave;
   const long nrows = (long)G.B * G.T * G.Hq;
   if (row_id >= nrows) return;
   const int h = (int)(row_id % G.Hq);
@@ -57,64 +107,249 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   const int b = (int)(row_id / ((long)G.Hq * G.T));
   const int kv = h / G.G;
   const int r = i * G.G + (h % G.G);
-  float* outp = a.out + row_id * D;
-  float* lsep = a.lse + ((size_t)b * G.Hq + h) * G.T + i;
+  const int T = G.T;
+  float* outp = a.out + row_id * D + DPL * dl;
+  float* lsep = a.lse + ((size_t)b * G.Hq + h) * T + i;
+  const size_t base = ((size_t)b * G.Hkv + kv) * (G.S + 1);
+  const float* lrow = a.lse_part + base * G.R_pad + r;                 // slot s at s * R_pad
+  const float* orow = a.o_part + (base * G.R_pad + r) * D + DPL * dl;  // slot s at s * R_pad * D
+  const size_t ostride = (size_t)G.R_pad * D;
+  const bool tree_slot = !FUSED && a.include_tree;  // the plain merge's tree partial
 
+  // ---- issue the loads
   const int Lb = a.prefix_len[b];
-  const bool bad = Lb < 0 || Lb > G.Lmax || (a.status && a.status[b] != 0);
-  if (bad) {
+  const int st = (!FUSED && a.status) ? a.status[b] : 0;
+  const float lse_lane = lane < G.S ? lrow[(size_t)lane * G.R_pad] : -INFINITY;
+  const float lse_tree = tree_slot ? lrow[(size_t)G.S * G.R_pad] : -INFINITY;
+  float4 vt[NV];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) outp[lane + 64 * e] = NAN;
+  for (int j = 0; j < NV; ++j) vt[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (tree_slot && pg == 0)
+#pragma unroll
+    for (int j = 0; j < NV; ++j) vt[j] = ((const float4*)(orow + (size_t)G.S * ostride))[j];
+  int par[kMaxT / 64];
+  float qv[DPL];
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int k = 0; k < kMaxT / 64; ++k) {
+      const int j = lane + 64 * k;
+      par[k] = j < T ? a.parent_idx[(size_t)b * T + j] : -1;
+    }
+    const unsigned short* qp = a.q + (size_t)row_id * D + DPL * dl;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) qv[e] = bf16_to_f32(qp[e]);
+  }
+  float lk[kBatch];
+  float4 v[kBatch][NV];
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const int p = pg + 4 * k;
+    lk[k] = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) v[k][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p < G.S) {
+      lk[k] = lrow[(size_t)p * G.R_pad];
+#pragma unroll
+      for (int j = 0; j < NV; ++j) v[k][j] = ((const float4*)(orow + (size_t)p * ostride))[j];
+    }
+  }
+
+  // ---- validate
+  bool bad = Lb < 0 || Lb > G.Lmax || st != 0;
+  if constexpr (FUSED) {
+    // parent pointers: parent[j] in [-1, j-1] for every node (the tree is topologically
+    // ordered); the verdict is wave-uniform
+    int bad_lane = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxT / 64; ++k) {
+      const int j = lane + 64 * k;
+      if (j < T) {
+        bad_lane |= (par[k] < -1 || par[k] >= j) ? 1 : 0;
+        s_par[wave][j] = par[k];
+      }
+    }
+    const bool tree_bad = __builtin_amdgcn_ballot_w64(bad_lane != 0) != 0;
+    const bool len_bad = Lb < 0 || Lb > G.Lmax;
+    if (i == 0 && h == 0 && lane == 0)
+      a.status_out[b] = (tree_bad ? kStatusTree : 0) | (len_bad ? kStatusPrefixLen : 0);
+    bad = tree_bad || len_bad;
+  }
+  if (bad) {
+    if (pg == 0)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) outp[e] = NAN;
     if (lane == 0) *lsep = NAN;
     return;
   }
-  const int nsplit = (Lb + G.chunk - 1) / G.chunk;
-  const size_t slot0 = ((size_t)b * G.Hkv + kv) * (G.S + 1);
-  // parts: prefix splits 0..nsplit-1, then (optionally) the tree partial at slot S
-  const int nparts = nsplit + (a.include_tree ? 1 : 0);
-  auto part_slot = [&](int p) { return slot0 + (p < nsplit ? p : G.S); };
 
-  float M = -INFINITY;
-  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, a.lse_part[part_slot(p) * G.R_pad + r]);
-  M = wave_max(M);
-  if (M == -INFINITY) {  // no visible key at all (prefix-only merge of an empty prefix)
+  // ---- fused: the tree part over the visible keys i, parent(i), ... (log2 units)
+  float mt = -INFINITY, lt = 0.f;  // running maximum, this group's weight sum
+  float at[DPL];                   // this group's weighted value sum
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) outp[lane + 64 * e] = 0.f;
+  for (int e = 0; e < DPL; ++e) at[e] = 0.f;
+  if constexpr (FUSED) {
+    __builtin_amdgcn_wave_barrier();  // s_par written by this wave is read below
+    const float c = G.scale * kLog2e;
+    const unsigned short* Kt = a.k_tree + ((size_t)b * G.Hkv + kv) * (size_t)T * D + DPL * dl;
+    const unsigned short* Vt = a.v_tree + ((size_t)b * G.Hkv + kv) * (size_t)T * D + DPL * dl;
+    // one batch of keys, one per part group (key < 0: none): score, then online softmax
+    auto batch = [&](int my, const float (&kv8)[DPL], const float (&vv)[DPL]) {
+      float sc = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) sc += qv[e] * kv8[e];
+      sc = lane16_sum(sc) * c;
+      if (my < 0) sc = -INFINITY;
+      // finite: the first batch holds the row's own node; later ones start at a valid key
+      const float m_new = fmaxf(mt, group_max4(sc));
+      const float alpha = __builtin_amdgcn_exp2f(mt - m_new);
+      const float p = __builtin_amdgcn_exp2f(sc - m_new);
+      mt = m_new;
+      lt = lt * alpha + p;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) at[e] = at[e] * alpha + p * vv[e];
+    };
+    auto load_key = [&](int my, float (&kv8)[DPL], float (&vv)[DPL]) {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) kv8[e] = vv[e] = 0.f;
+      if (my >= 0) {
+        const unsigned short* kp = Kt + (size_t)my * D;
+        const unsigned short* vp = Vt + (size_t)my * D;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) {
+          kv8[e] = bf16_to_f32(kp[e]);
+          vv[e] = bf16_to_f32(vp[e]);
+        }
+      }
+    };
+    // the first eight keys of the chain (enough for trees up to depth 7) are found first and
+    // their K/V rows loaded together: one memory round trip
+    int t = i;  // next ancestor (wave-uniform); the chain ends at a root (parent -1)
+    int my0 = -1, my1 = -1;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      if (pg == (g & 3)) {
+        if (g < 4) my0 = t;
+        else my1 = t;
+      }
+      if (t >= 0) t = __builtin_amdgcn_readfirstlane(s_par[wave][t]);
+    }
+    {
+      float k0[DPL], v0[DPL], k1[DPL], v1[DPL];
+      load_key(my0, k0, v0);
+      load_key(my1, k1, v1);
+      batch(my0, k0, v0);
+      if (__builtin_amdgcn_ballot_w64(my1 >= 0) != 0) batch(my1, k1, v1);  // wave-uniform
+    }
+    while (t >= 0) {  // deeper chains, four keys at a time
+      int my = -1;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if (pg == g) my = t;
+        if (t >= 0) t = __builtin_amdgcn_readfirstlane(s_par[wave][t]);
+      }
+      float kk[DPL], vv[DPL];
+      load_key(my, kk, vv);
+      batch(my, kk, vv);
+    }
+  }
+
+  // ---- weights against the largest log-sum-exp (log2 units)
+  const int nsplit = (Lb + G.chunk - 1) / G.chunk;  // non-empty prefix splits
+  float M = fmaxf(lane < nsplit ? lse_lane * kLog2e : -INFINITY, lse_tree * kLog2e);
+  for (int p = 64 + lane; p < nsplit; p += 64) M = fmaxf(M, lrow[(size_t)p * G.R_pad] * kLog2e);
+  M = wave_max(M);
+  float ltot = 0.f;
+  if constexpr (FUSED) {
+    ltot = group_sum4(lt);                 // the tree's weight sum relative to mt
+    M = fmaxf(M, mt + __log2f(ltot));      // the tree part's log-sum-exp
+  }
+  if (M == -INFINITY) {  // no visible key at all (prefix-only merge of an empty prefix)
+    if (pg == 0)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) outp[e] = 0.f;
     if (lane == 0) *lsep = -INFINITY;
     return;
   }
   float acc[DPL];
+  float wl = 0.f;  // this group's weight sum
+  {
+    const float wt = (tree_slot && pg == 0) ? __builtin_amdgcn_exp2f(lse_tree * kLog2e - M) : 0.f;
+    wl += wt;
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-  float wsum = 0.f;
-  for (int p0 = 0; p0 < nparts; p0 += 64) {
-    const int p = p0 + lane;
-    float w = 0.f;
-    if (p < nparts) {
-      const float l = a.lse_part[part_slot(p) * G.R_pad + r];
-      w = __builtin_amdgcn_exp2f((l - M) * kLog2e);
-    }
-    wsum += w;
-    const int cnt = min(64, nparts - p0);
-    for (int k = 0; k < cnt; ++k) {
-      const float wk = __shfl(w, k);
-      const float* op = a.o_part + (part_slot(p0 + k) * G.R_pad + r) * D;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] += wk * op[lane + 64 * e];
+    for (int j = 0; j < NV; ++j) {
+      acc[4 * j + 0] = wt * vt[j].x;
+      acc[4 * j + 1] = wt * vt[j].y;
+      acc[4 * j + 2] = wt * vt[j].z;
+      acc[4 * j + 3] = wt * vt[j].w;
     }
   }
-  wsum = wave_sum(wsum);
-  const float inv = 1.f / wsum;
+  auto add_part = [&](float l, const float4 (&pv)[NV]) {
+    const float w = __builtin_amdgcn_exp2f(l * kLog2e - M);
+    wl += w;
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) outp[lane + 64 * e] = acc[e] * inv;
-  if (lane == 0) *lsep = M + __logf(wsum);
+    for (int j = 0; j < NV; ++j) {
+      acc[4 * j + 0] += w * pv[j].x;
+      acc[4 * j + 1] += w * pv[j].y;
+      acc[4 * j + 2] += w * pv[j].z;
+      acc[4 * j + 3] += w * pv[j].w;
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k)
+    if (pg + 4 * k < nsplit) add_part(lk[k], v[k]);
+  // splits beyond the first 36 (long prefixes with many splits)
+  for (int p0 = 4 * kBatch + pg; p0 < nsplit; p0 += 4 * kBatch) {
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int p = p0 + 4 * k;
+      if (p < nsplit) {
+        lk[k] = lrow[(size_t)p * G.R_pad];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) v[k][j] = ((const float4*)(orow + (size_t)p * ostride))[j];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (p0 + 4 * k < nsplit) add_part(lk[k], v[k]);
+  }
+  float wsum = group_sum4(wl);
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = group_sum4(acc[e]);
+  if constexpr (FUSED) {
+    const float wt = __builtin_amdgcn_exp2f(mt - M);
+    wsum += wt * ltot;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] += wt * group_sum4(at[e]);
+  }
+  const float inv = 1.f / wsum;
+  if (pg == 0) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      ((float4*)outp)[j] = make_float4(acc[4 * j] * inv, acc[4 * j + 1] * inv,
+                                       acc[4 * j + 2] * inv, acc[4 * j + 3] * inv);
+  }
+  if (lane == 0) *lsep = (M + __log2f(wsum)) * kLn2;
+}
+
+template <bool FUSED>
+hipError_t launch_merge(const MergeArgs& a, const Geometry& g, hipStream_t stream) {
+  const long nrows = (long)g.B * g.T * g.Hq;
+  const int rows_per_block = kThreads / 64;
+  dim3 grid((unsigned)((nrows + rows_per_block - 1) / rows_per_block));
+  if (g.D == 128)
+    hipLaunchKernelGGL((lse_merge<128, FUSED>), grid, dim3(kThreads), 0, stream, a);
+  else if (g.D == 64)
+    hipLaunchKernelGGL((lse_merge<64, FUSED>), grid, dim3(kThreads), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_lse_merge(const Geometry& g, const int32_t* prefix_len, bool include_tree,
                             float* out, float* lse, const Workspace& ws, hipStream_t stream) {
-  MergeArgs a;
+  MergeArgs a = {};
   a.prefix_len = prefix_len;
   a.status = include_tree ? ws.status : nullptr;
   a.lse_part = ws.lse_part;
@@ -123,16 +358,27 @@ hipError_t launch_lse_merge(const Geometry& g, const int32_t* prefix_len, bool i
   a.lse = lse;
   a.g = g;
   a.include_tree = include_tree ? 1 : 0;
-  const long nrows = (long)g.B * g.T * g.Hq;
-  const int rows_per_block = kThreads / 64;
-  dim3 grid((unsigned)((nrows + rows_per_block - 1) / rows_per_block));
-  if (g.D == 128)
-    hipLaunchKernelGGL(lse_merge<128>, grid, dim3(kThreads), 0, stream, a);
-  else if (g.D == 64)
-    hipLaunchKernelGGL(lse_merge<64>, grid, dim3(kThreads), 0, stream, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  return launch_merge<false>(a, g, stream);
+}
+
+hipError_t launch_tree_merge(const Geometry& g, const void* q, const void* k_tree,
+                             const void* v_tree, const int32_t* parent_idx,
+                             const int32_t* prefix_len, float* out, float* lse,
+                             const Workspace& ws, hipStream_t stream) {
+  MergeArgs a = {};
+  a.prefix_len = prefix_len;
+  a.lse_part = ws.lse_part;
+  a.o_part = ws.o_part;
+  a.out = out;
+  a.lse = lse;
+  a.q = (const unsigned short*)q;
+  a.k_tree = (const unsigned short*)k_tree;
+  a.v_tree = (const unsigned short*)v_tree;
+  a.parent_idx = parent_idx;
+  a.status_out = ws.status;
+  a.g = g;
+  a.include_tree = 1;
+  return launch_merge<true>(a, g, stream);
 }
 
 }  // namespace hta

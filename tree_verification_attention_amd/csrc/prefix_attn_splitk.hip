@@ -44,6 +44,7 @@
 //    (exact for |v| in [2^-14, 65504]), and the normaliser sums the unrounded fp32
 //    probabilities.
 #include "hta_internal.h"
+#include "lds_tiles.h"
 
 #include <type_traits>
 
@@ -53,7 +54,6 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kKeyTile = 64;
 constexpr int kKStages = 4;  // K ring: tile t (scores), t+1 (landed), t+2, t+3 (in flight)
 constexpr int kVStages = 3;  // V ring: tile t+1 (being transposed), t+2, t+3 (in flight)
 constexpr int kVtStages = 3;  // V^T: tiles t-1 (second wave group), t (consumed), t+1 (made)
@@ -75,31 +75,9 @@ struct Layout {
   static constexpr int kBytes = kVt + kVtStages * kTileBytes;
 };
 
-// XOR swizzles of the 16-byte chunk index within a row.
-//  K rows (D bf16) are read 16 at a time at one chunk column: D = 128 uses chunk ^ row%16,
-//    which spreads the 16 rows over all 64 banks.
-//  V rows (D bf16) are read 4 at a time over two chunk columns by the transposing read:
-//    chunk ^ 2*(row%8) keeps the 4 rows x 2 chunks of one 16-lane block on distinct banks.
-//  V^T rows (one per d, 64 keys fp16 = 8 chunks) are read 16 at a time at one chunk column:
-//    chunk ^ (row/2)%8 (rows 2m and 2m+1 sit in opposite bank halves).
-template <int D>
-__device__ __forceinline__ int swz_k(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-template <int D>
-__device__ __forceinline__ int swz_v(int row) {
-  return D == 128 ? 2 * (row & 7) : 2 * (row & 3);
-}
+// V^T rows (one per d, 64 keys fp16 = 8 chunks) are read 16 at a time at one chunk column:
+// chunk ^ (row/2)%8 (rows 2m and 2m+1 sit in opposite bank halves).
 __device__ __forceinline__ int swz_vt(int d) { return (d >> 1) & 7; }
-
-// One 16-byte-per-lane direct load from global memory into LDS: lane l's 16 bytes land at
-// lds + 16 l (global_load_lds_dwordx4).  The builtin only exists for the device; the host
-// pass parses this body without generating it.
-__device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
-#endif
-}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -226,18 +204,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
 
   // ---- stream K/V tiles into the LDS rings
   auto issue = [&](int t) {
-    unsigned char* ks = lds + Y::kKRing + (t % kKStages) * Y::kTileBytes;
-    unsigned char* vs = lds + Y::kVRing + (t % kVStages) * Y::kTileBytes;
-    const int key0 = kbeg + t * kKeyTile;
-#pragma unroll
-    for (int j = 0; j < DPW; ++j) {
-      const int blk = j * 4 + ww;         // 1 KB block of the tile written by this wave
-      const int u = 64 * blk + lane;      // 16-byte chunk position within the tile
-      const int r = u / Y::kChunks, p = u % Y::kChunks;
-      const size_t gk = (size_t)min(key0 + r, kend - 1);
-      lds_dma16(Kg + gk * D + 8 * (p ^ swz_k<D>(r)), ks + 1024 * blk);
-      lds_dma16(Vg + gk * D + 8 * (p ^ swz_v<D>(r)), vs + 1024 * blk);
-    }
+    dma_kv_tile<D, 4>(Kg, Vg, kbeg + t * kKeyTile, kend,
+                      lds + Y::kKRing + (t % kKStages) * Y::kTileBytes,
+                      lds + Y::kVRing + (t % kVStages) * Y::kTileBytes, ww, lane);
   };
 
   // ---- V (bf16, keys x d) -> V^T (fp16, d x keys in P^T operand order).  Lane (grp, l16)

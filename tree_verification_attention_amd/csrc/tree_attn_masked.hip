@@ -12,20 +12,30 @@
 // sets M_i |= M_{a_i} and a_i = a_{a_i}, doubling the covered path length, until every
 // jump pointer reaches the root.  ceil(log2(depth + 1)) rounds; bit-exact.
 //
-// Attention.  One wave per query row: the lanes that own a visible key compute its score,
-// the wave reduces max and sum, and the lanes then own output dimensions and accumulate
-// the visible values.  All fp32 on exactly widened bf16 inputs.  The result is the tree
-// partial (slot S of the partial buffers), merged with the prefix partials by lse_merge.
+// Attention on the matrix cores, one wave per 16-row tile (rows r = node*G + head-in-group
+// of one KV head, as in the prefix pass).  The workgroup streams the sequence's tree K and V
+// rows of its KV head into LDS with direct loads issued first thing, and loads its query
+// operands, so their latency overlaps the mask construction.  Scores are formed transposed,
+// S^T = K Q^T (v_mfma_f32_16x16x32_bf16), masked with the lane's node mask, and turned into
+// probabilities against a per-row running maximum over 64-key tiles (at most four tiles:
+// T <= 256).  The output is O^T += V^T P^T (v_mfma_f32_16x16x32_f16) with V^T operands read
+// by transposing reads (ds_read_b64_tr_b16) and widened from bf16 to fp16 in registers;
+// probabilities (at most 1) enter as fp16, the normaliser sums them unrounded in fp32.  The
+// result is the tree partial (slot S of the partial buffers), merged with the prefix
+// partials by lse_merge.
 #include "hta_internal.h"
+#include "lds_tiles.h"
 
 namespace hta {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 4;  // one 16-row tile per wave
+constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxT = 256;
 constexpr int kMaxW = kMaxT / 64;
-constexpr int kRowsPerWave = 2;
+
+typedef __attribute__((ext_vector_type(4))) short i16x4;
 
 struct TreeArgs {
   const unsigned short* q;        // bf16 [B, T, Hq, D]
@@ -41,40 +51,82 @@ struct TreeArgs {
   int32_t attention;              // 0: masks and status only
 };
 
-__device__ inline float bf16_to_f32(unsigned short h) {
-  return __builtin_bit_cast(float, (uint32_t)h << 16);
+__device__ inline _Float16 bf16_bits_to_f16(short h) {
+  return (_Float16)__builtin_bit_cast(float, (uint32_t)(unsigned short)h << 16);
 }
 
-__device__ inline float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+// lanes l, l^16, l^32, l^48 hold the same query row
+__device__ inline float group_max(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float group_sum(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__device__ inline float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
-// Grid: x = row block of kRowsPerWave*4 rows, y = kv head, z = sequence.
+// Grid: x = group of kWaves row tiles, y = kv head, z = sequence.
 template <int D>
 __global__ __launch_bounds__(kThreads) void tree_attn_masked(TreeArgs a) {
+  constexpr int DS = D / 32;          // 32-wide d steps of the score product
+  constexpr int DB = D / 16;          // 16-wide d blocks of the output
   __shared__ uint64_t s_mask[kMaxT][kMaxW];
   __shared__ int32_t s_jump[kMaxT];
-  __shared__ float s_p[kThreads / 64][kMaxT];
+  // K and V tiles of the sequence's tree keys: dynamic LDS of 2 * ceil(T / 64) tiles
+  extern __shared__ __attribute__((aligned(1024))) unsigned char s_kv[];
   const Geometry& G = a.g;
   const int b = blockIdx.z, kv = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, grp = lane >> 4;
   const int T = G.T, W = G.W;
+  constexpr int kTileBytes = kKeyTile * D * 2;
+  const int ntile = (T + kKeyTile - 1) / kKeyTile;
+  unsigned char* s_k = s_kv;
+  unsigned char* s_vv = s_kv + ntile * kTileBytes;
+  const unsigned short* Kt = a.k_tree + ((size_t)b * G.Hkv + kv) * (size_t)T * D;
+  const unsigned short* Vt = a.v_tree + ((size_t)b * G.Hkv + kv) * (size_t)T * D;
+  const int rt = blockIdx.x * kWaves + wave;  // this wave's row tile
+  const int row = rt * 16 + l16;
+  const bool row_ok = rt < G.NT && row < G.R;
+  const int node = row_ok ? row / G.G : 0;
+  const int head = kv * G.G + (row_ok ? row % G.G : 0);
+  // parent pointers first: their latency then overlaps the issue of everything else
+  const int par = tid < T ? a.parent_idx[(size_t)b * T + tid] : -1;
+  bf16x8 qop[DS];
+  if (a.attention) {
+    // issue every global read of the attention up front: K/V tiles straight into LDS,
+    // this wave's query operands (B of S^T: Q[row = l16][d = 32 ds + 8 grp ..]) into
+    // registers; padding rows read zeros
+    for (int t = 0; t < ntile; ++t)
+      dma_kv_tile<D, kWaves, true>(Kt, Vt, t * kKeyTile, T, s_k + t * kTileBytes,
+                                   s_vv + t * kTileBytes, wave, lane);
+    // V rows of the blocks left out (past T, up to the end of the last tile) must hold
+    // finite values: they meet probability 0 in the PV product.  K rows there stay
+    // undefined; their scores are masked before use.
+    constexpr int kRowsPerBlock = 1024 / (2 * D);
+    const int zrow = (T + kRowsPerBlock - 1) / kRowsPerBlock * kRowsPerBlock;
+    for (int u = zrow * (2 * D / 16) + tid; u < ntile * kKeyTile * (2 * D / 16); u += kThreads)
+      *(uint4*)(s_vv + 16 * u) = make_uint4(0, 0, 0, 0);
+    const unsigned short* qp = a.q + (((size_t)b * T + node) * G.Hq + head) * D + 8 * grp;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const uint4 v = row_ok ? *(const uint4*)(qp + 32 * ds) : make_uint4(0, 0, 0, 0);
+      qop[ds] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
 
   // ---- load and validate parent pointers; seed the pointer-jumping state
   int bad = 0;
-  for (int i = tid; i < T; i += kThreads) {
-    const int p = a.parent_idx[(size_t)b * T + i];
-    const bool ok = p >= -1 && p < i;
-    bad |= ok ? 0 : 1;
-    s_jump[i] = ok ? p : -1;
+  if (tid < T) {  // T <= kThreads: thread i owns node i
+    const int i = tid;
+    const bool ok = par >= -1 && par < i;
+    bad = ok ? 0 : 1;
+    s_jump[i] = ok ? par : -1;
     for (int w = 0; w < W; ++w) s_mask[i][w] = (w == (i >> 6)) ? (1ull << (i & 63)) : 0ull;
   }
   const int tree_bad = __syncthreads_or(bad);
@@ -111,77 +163,107 @@ __global__ __launch_bounds__(kThreads) void tree_attn_masked(TreeArgs a) {
   }
   if (!a.attention) return;
 
-  // ---- masked attention, one wave per row
+  // the tiles have landed (this wave's loads) and are visible (barrier)
+  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+  __syncthreads();
+
+  if (rt >= G.NT) return;
   const size_t slot = ((size_t)b * G.Hkv + kv) * (G.S + 1) + G.S;
-  const unsigned short* Kt = a.k_tree + ((size_t)b * G.Hkv + kv) * (size_t)T * D;
-  const unsigned short* Vt = a.v_tree + ((size_t)b * G.Hkv + kv) * (size_t)T * D;
-  constexpr int DPL = D / 64;  // output dims per lane
-  for (int rr = 0; rr < kRowsPerWave; ++rr) {
-    const int row = (blockIdx.x * (kThreads / 64) + wave) * kRowsPerWave + rr;
-    if (row >= G.R) break;
-    const int node = row / G.G;
-    const int head = kv * G.G + row % G.G;
-    const unsigned short* qp = a.q + (((size_t)b * T + node) * G.Hq + head) * D;
-    float* op = a.o_part + (slot * G.R_pad + row) * D;
-    if (tree_bad) {
-      for (int d = lane; d < D; d += 64) op[d] = NAN;
-      if (lane == 0) a.lse_part[slot * G.R_pad + row] = NAN;
-      continue;
-    }
-    // scores of the visible keys (lane t%64 owns key t)
-    float mx = -INFINITY;
-    for (int t0 = 0; t0 < T; t0 += 64) {
-      const int t = t0 + lane;
-      float s = -INFINITY;
-      if (t < T && ((s_mask[node][t >> 6] >> (t & 63)) & 1ull)) {
-        const uint4* kp = (const uint4*)(Kt + (size_t)t * D);
-        const uint4* q4 = (const uint4*)qp;
-        float dot = 0.f;
-#pragma unroll 4
-        for (int c = 0; c < D / 8; ++c) {
-          const uint4 kk = kp[c], qq = q4[c];
-          const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
-          const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
+  float* op = a.o_part + (slot * G.R_pad + row) * D + 4 * grp;
+  if (tree_bad) {
+    if (row_ok) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            dot += bf16_to_f32(qw[e] & 0xffff) * bf16_to_f32(kw[e] & 0xffff);
-            dot += bf16_to_f32(qw[e] >> 16) * bf16_to_f32(kw[e] >> 16);
-          }
-        }
-        s = dot * G.scale;
-      }
-      if (t < T) s_p[wave][t] = s;
-      mx = fmaxf(mx, s);
+      for (int db = 0; db < DB; ++db)
+        *(f32x4*)(op + 16 * db) = f32x4{NAN, NAN, NAN, NAN};
+      if (grp == 0) a.lse_part[slot * G.R_pad + row] = NAN;
     }
-    mx = wave_max(mx);  // finite: node itself is always visible
-    float z = 0.f;
-    for (int t = lane; t < T; t += 64) {
-      const float s = s_p[wave][t];
-      const float p = (s == -INFINITY) ? 0.f : __expf(s - mx);
-      s_p[wave][t] = p;
-      z += p;
-    }
-    z = wave_sum(z);
-    __builtin_amdgcn_wave_barrier();
-    float o[DPL];
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-    for (int w = 0; w < W; ++w) {
-      uint64_t bits = s_mask[node][w];
-      while (bits) {
-        const int t = w * 64 + __builtin_ctzll(bits);
-        bits &= bits - 1;
-        const float p = s_p[wave][t];
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) o[e] += p * bf16_to_f32(Vt[(size_t)t * D + lane + 64 * e]);
-      }
-    }
-    const float inv = 1.f / z;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) op[lane + 64 * e] = o[e] * inv;
-    if (lane == 0) a.lse_part[slot * G.R_pad + row] = mx + __logf(z);
-    __builtin_amdgcn_wave_barrier();
+    return;
   }
+
+  const float c = G.scale * kLog2e;
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = zero4;
+  float m_run = -INFINITY, l_run = 0.f;
+  // V^T operand lanes: d = 16 db + l16, keys 32 h + 16 (e / 4) + 4 grp + e % 4
+  const int vrow = 4 * grp + (l16 >> 2);
+  const int vch = (l16 & 3) >> 1, vhalf = 8 * (l16 & 1);
+
+  for (int tile = 0; tile < ntile; ++tile) {
+    // ---- scores of keys 64 tile + 16 kb + 4 grp + i (keys past T re-read key T-1, masked)
+    const unsigned char* Ks = s_k + tile * kTileBytes;
+    f32x4 sc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int kr = kb * 16 + l16;
+      sc[kb] = zero4;
+      if (tile * kKeyTile + kb * 16 >= T) continue;  // no key of this block exists
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        const bf16x8 kop =
+            *(const bf16x8*)(Ks + kr * (2 * D) + 16 * ((4 * ds + grp) ^ swz_k<D>(kr)));
+        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[ds], sc[kb], 0, 0, 0);
+      }
+    }
+    // ---- ancestor-or-self mask of this lane's node (key t visible iff bit t is set)
+    const uint64_t mw = s_mask[node][tile];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = kb * 16 + 4 * grp + i;
+        const float x = ((mw >> k) & 1ull) ? sc[kb][i] * c : -INFINITY;
+        sc[kb][i] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    const float m_new = fmaxf(m_run, group_max(tmax));
+    // a row may see no key of this tile (and none before): keep its state at zero
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (tile * kKeyTile + 32 * h >= T) break;  // no key of this half exists
+      // P^T operand of the 32-key half h: element e <-> key 32 h + 16 (e / 4) + 4 grp + e % 4
+      f16x8 pop;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(sc[2 * h + e / 4][e % 4] - m_use);
+        l_run += p;
+        pop[e] = (_Float16)p;
+      }
+      const unsigned char* Vs = s_vv + tile * kTileBytes;
+      const int r0 = 32 * h + vrow, r1 = r0 + 16;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int ch = 2 * db + vch;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(
+            Vs + r0 * (2 * D) + 16 * (ch ^ swz_v<D>(r0)) + vhalf));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(
+            Vs + r1 * (2 * D) + 16 * (ch ^ swz_v<D>(r1)) + vhalf));
+        f16x8 vop;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vop[e] = bf16_bits_to_f16(lo[e]);
+          vop[4 + e] = bf16_bits_to_f16(hi[e]);
+        }
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop, acc[db], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- normalise and write the tree partial (every real row sees at least itself)
+  const float lt = group_sum(l_run);
+  if (!row_ok) return;
+  const float inv = 1.f / lt;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) *(f32x4*)(op + 16 * db) = acc[db] * inv;
+  if (grp == 0) a.lse_part[slot * G.R_pad + row] = (m_run + __log2f(lt)) * kLn2;
 }
 
 }  // namespace
@@ -202,13 +284,22 @@ hipError_t launch_tree_attn_masked(const Geometry& g, const void* q, const void*
   a.o_part = ws.o_part;
   a.g = g;
   a.attention = attention ? 1 : 0;
-  const int rows_per_block = kRowsPerWave * (kThreads / 64);
-  const int xblocks = attention ? (g.R + rows_per_block - 1) / rows_per_block : 1;
+  const int xblocks = attention ? (g.NT + kWaves - 1) / kWaves : 1;
   dim3 grid(xblocks, attention ? g.Hkv : 1, g.B);
+  // K and V staging: ceil(T / 64) tiles each (none when only the masks are built)
+  const size_t shmem = attention ? (size_t)2 * ((g.T + 63) / 64) * 64 * 2 * g.D : 0;
+  if (shmem > 65536) {  // above the default dynamic-LDS limit (T > 128 at D = 128)
+    const hipError_t e = g.D == 128
+        ? hipFuncSetAttribute((const void*)tree_attn_masked<128>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem)
+        : hipFuncSetAttribute((const void*)tree_attn_masked<64>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+  }
   if (g.D == 128)
-    hipLaunchKernelGGL(tree_attn_masked<128>, grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(tree_attn_masked<128>, grid, dim3(kThreads), shmem, stream, a);
   else if (g.D == 64)
-    hipLaunchKernelGGL(tree_attn_masked<64>, grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(tree_attn_masked<64>, grid, dim3(kThreads), shmem, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
