@@ -34,9 +34,9 @@
  * takes a caller-allocated device workspace of at least hta_workspace_size() bytes and a
  * HIP stream (passed as void*, a hipStream_t; NULL = the default stream).  Calls are
  * asynchronous: a return of HTA_OK means the work was enqueued on the stream.  The library
- * keeps no mutable global state beyond a per-device cache of the compute-unit count, so
- * calls on different streams with different workspaces may run concurrently; calls that
- * share a workspace must be ordered by the caller.
+ * keeps no mutable global state (plans are a pure function of the descriptor), so calls on
+ * different streams with different workspaces may run concurrently; calls that share a
+ * workspace must be ordered by the caller.
  *
  * Errors.  Every argument check happens on the host before anything is enqueued; on an
  * error the call returns a non-zero hta_status and enqueues nothing.  Errors only visible on
@@ -46,7 +46,9 @@
  *
  * Limits: head_dim in {64, 128}; 1 <= tree_size <= 256; num_q_heads % num_kv_heads == 0;
  * num_q_heads / num_kv_heads <= 16; every tensor pointer 16-byte aligned, the workspace
- * 256-byte aligned; in_dtype HTA_BF16.
+ * 256-byte aligned.  in_dtype HTA_BF16 runs the matrix-core kernels (bf16 products, fp32
+ * accumulation, probabilities entering the PV product as fp16); HTA_F32 runs exact fp32
+ * vector-ALU kernels meant for small validation shapes (same plan, workspace and layouts).
  */
 #ifndef HTA_H
 #define HTA_H
@@ -113,9 +115,12 @@ hta_status hta_plan(const hta_desc *desc, hta_plan_info *info);
 size_t hta_workspace_size(const hta_desc *desc);
 
 /*
- * The whole verification attention step: ancestor masks, tree partial, split-K prefix
- * partials, LSE merge -> out, lse.  The exact aggregation of the prefix and tree parts
- * (README, Introduction; summary, Summary; arXiv abstract).
+ * The whole verification attention step -> out, lse: the split-K prefix partials, then the
+ * exact LSE aggregation with the tree part (README, Introduction; summary, Summary; arXiv
+ * abstract).  Two launches: the prefix pass, and a merge that computes each row's tree
+ * attention over its node's parent chain itself (validating the trees and recording the
+ * device status) instead of reading a tree partial; the ancestor masks are not materialised
+ * here (hta_ancestor_masks builds them).  The workspace partial buffers are overwritten.
  */
 hta_status hta_verify(const hta_desc *desc, const void *q, const void *k_prefix,
                       const void *v_prefix, const void *k_tree, const void *v_tree,

@@ -78,13 +78,20 @@ def test_plan_llama_shape():
     (dict(chunk=100), SHAPE),               # not a multiple of 64
     (dict(scale=-1.0), SHAPE),
     (dict(scale=float("nan")), SHAPE),
-    (dict(in_dtype=1), DTYPE),
+    (dict(in_dtype=2), DTYPE),
     (dict(in_dtype=7), DTYPE),
 ])
 def test_bad_descriptors_are_rejected(kw, code):
     d = _desc(**kw)
     assert _plan_code(d) == code
     assert hta.workspace_size(d) == 0
+
+
+def test_fp32_inputs_plan_like_bf16():
+    # fp32 inputs take their own kernels but the same plan, workspace and partial layout
+    a, b = hta.plan(_desc()), hta.plan(_desc(in_dtype=1))
+    for f in ("chunk", "num_splits", "rows", "rows_padded", "workspace_bytes"):
+        assert getattr(a, f) == getattr(b, f)
 
 
 def test_null_descriptor():

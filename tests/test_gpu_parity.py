@@ -98,10 +98,11 @@ def test_ancestor_masks_bit_exact(T):
 # ----------------------------------------------------------------------------- the parts
 
 
-def _small(name, parents, *, B=2, Hq=8, Hkv=2, D=128, L=1000, plen=None, seed=0, peaky=0.02):
+def _small(name, parents, *, B=2, Hq=8, Hkv=2, D=128, L=1000, plen=None, seed=0, peaky=0.02,
+           dtype=torch.bfloat16):
     return W.make_workload(name, batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
                            max_prefix_len=L, parents=parents, prefix_len=plen, seed=seed,
-                           peaky_frac=peaky)
+                           peaky_frac=peaky, dtype=dtype)
 
 
 def test_tree_part_alone_prefix_len_zero():
@@ -309,3 +310,66 @@ def test_prefix_len_out_of_range_is_flagged():
     code, seq = hta.hta_get_device_status(desc, ws)
     assert code == 7 and seq == 1
     assert np.all(np.isnan(out[1].cpu().numpy())) and np.all(np.isfinite(out[0].cpu().numpy()))
+
+
+# ----------------------------------------------------------------------------- fp32 inputs
+
+F32_TOL = 2e-5  # exact fp32 arithmetic against the fp64 oracle
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 4])
+def test_fp32_verify(D, G):
+    gen = torch.Generator().manual_seed(40 + G + D)
+    par = [W.level_tree(W.LONGSPEC_TREE_WIDTHS, gen), W.chain_tree(68)]
+    w = _small(f"f32_D{D}_G{G}", par, B=2, Hq=2 * G, Hkv=2, D=D, L=700, plen=[700, 129],
+               seed=41 + G + D, dtype=torch.float32)
+    _log(f"fp32 verify D={D} G={G}")
+    out, lse = run_gpu(w, chunk=256)
+    check_rows(w, out, lse, out_tol=F32_TOL, lse_tol=F32_TOL)
+
+
+def test_fp32_entry_points_match_oracle_parts():
+    """fp32 through the separate entry points: tree partial alone, prefix partials alone, the
+    plain merge, each against the oracle's part-wise attention."""
+    gen = torch.Generator().manual_seed(50)
+    par = [W.random_forest(130, gen)]
+    w = _small("f32_parts", par, B=1, Hq=4, Hkv=2, D=64, L=600, plen=[577], seed=50,
+               dtype=torch.float32)
+    t = to_dev(w)
+    desc = hta.desc_for(t["q"], t["k_prefix"], w.scale, chunk=256)
+    ws = hta.new_workspace(desc, "cuda")
+    hta.hta_tree_partials(desc, t["q"], t["k_tree"], t["v_tree"], t["parent_idx"],
+                          t["prefix_len"], ws)
+    hta.hta_prefix_partials(desc, t["q"], t["k_prefix"], t["v_prefix"], t["prefix_len"], ws)
+    B, T, Hq, D = w.q.shape
+    out = torch.empty(B, T, Hq, D, device="cuda")
+    lse = torch.empty(B, Hq, T, device="cuda")
+    hta.hta_merge(desc, t["prefix_len"], True, out, lse, ws)
+    torch.cuda.synchronize()
+    assert hta.hta_get_device_status(desc, ws) == (0, -1)
+    check_rows(w, out.cpu().double().numpy(), lse.cpu().double().numpy(), out_tol=F32_TOL,
+               lse_tol=F32_TOL)
+    lse_p, o_p = (x.cpu().double().numpy() for x in hta.partial_views(desc, ws))
+    info = hta.plan(desc)
+    G = Hq // w.num_kv_heads
+    b_idx = np.zeros(T * Hq, dtype=np.int64)
+    h_idx = np.tile(np.arange(Hq), T)
+    i_idx = np.repeat(np.arange(T), Hq)
+    ro, rl = oracle.rows(w.as_numpy(), w.scale, b_idx, h_idx, i_idx, oracle.PART_TREE)
+    go = o_p[0, h_idx // G, info.num_splits, i_idx * G + h_idx % G]
+    gl = lse_p[0, h_idx // G, info.num_splits, i_idx * G + h_idx % G]
+    assert float(np.max(np.abs(go - ro))) <= F32_TOL
+    assert float(np.max(np.abs(gl - rl))) <= F32_TOL
+
+
+def test_fp32_invalid_tree_and_prefix_len():
+    gen = torch.Generator().manual_seed(51)
+    good = W.level_tree((2, 3), gen)
+    bad = list(good)
+    bad[2] = 2  # a node as its own parent
+    w = _small("f32_bad", [good, bad], B=2, Hq=2, Hkv=1, D=64, L=100, seed=51,
+               dtype=torch.float32)
+    out, lse = run_gpu(w)
+    assert np.all(np.isnan(out[1])) and np.all(np.isnan(lse[1]))
+    assert np.all(np.isfinite(out[0])) and np.all(np.isfinite(lse[0]))

@@ -30,7 +30,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 hta_status make_plan(const hta_desc* d, Geometry* g, hta_plan_info* info) {
   if (!d) return HTA_ERR_NULL;
-  if (d->in_dtype != HTA_BF16) return HTA_ERR_DTYPE;
+  if (d->in_dtype != HTA_BF16 && d->in_dtype != HTA_F32) return HTA_ERR_DTYPE;
   if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->tree_size < 1 ||
       d->tree_size > kMaxTree || d->max_prefix_len < 0 ||
       (d->head_dim != 64 && d->head_dim != 128) || d->num_q_heads % d->num_kv_heads != 0 ||
@@ -50,6 +50,7 @@ hta_status make_plan(const hta_desc* d, Geometry* g, hta_plan_info* info) {
   G.NT = G.R_pad / 16;
   G.W = (G.T + 63) / 64;
   G.scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)G.D);
+  G.f32 = d->in_dtype == HTA_F32 ? 1 : 0;
   int mt, tpb, nb;
   hta::prefix_row_blocking(G, &mt, &tpb, &nb);
   const int64_t row_blocks = nb;
@@ -117,6 +118,15 @@ hta_status check_ptrs(std::initializer_list<const void*> ptrs) {
 
 hta_status hip_status(hipError_t e) { return e == hipSuccess ? HTA_OK : HTA_ERR_HIP; }
 
+// The prefix pass for the descriptor's input dtype: bf16 on the matrix cores, fp32 on the
+// vector ALUs.
+hipError_t launch_prefix(const Geometry& G, const void* q, const void* k_prefix,
+                         const void* v_prefix, const int32_t* prefix_len, const Workspace& ws,
+                         hipStream_t s) {
+  return G.f32 ? hta::launch_prefix_attn_f32(G, q, k_prefix, v_prefix, prefix_len, ws, s)
+               : hta::launch_prefix_attn_splitk(G, q, k_prefix, v_prefix, prefix_len, ws, s);
+}
+
 #define HTA_TRY(expr)                  \
   do {                                 \
     hta_status _s = (expr);            \
@@ -151,8 +161,7 @@ hta_status hta_verify(const hta_desc* desc, const void* q, const void* k_prefix,
   const Workspace ws = carve(workspace, p);
   hipStream_t s = (hipStream_t)stream;
   // two launches: the split-K prefix pass, then the merge with the tree part fused in
-  HTA_TRY(hip_status(
-      hta::launch_prefix_attn_splitk(G, q, k_prefix, v_prefix, prefix_len, ws, s)));
+  HTA_TRY(hip_status(launch_prefix(G, q, k_prefix, v_prefix, prefix_len, ws, s)));
   return hip_status(hta::launch_tree_merge(G, q, k_tree, v_tree, parent_idx, prefix_len, out,
                                            lse, ws, s));
 }
@@ -182,8 +191,7 @@ hta_status hta_prefix_partials(const hta_desc* desc, const void* q, const void* 
   if (G.Lmax > 0) HTA_TRY(check_ptrs({k_prefix, v_prefix}));
   HTA_TRY(check_ws(p, workspace, workspace_bytes));
   const Workspace ws = carve(workspace, p);
-  return hip_status(hta::launch_prefix_attn_splitk(G, q, k_prefix, v_prefix, prefix_len, ws,
-                                                   (hipStream_t)stream));
+  return hip_status(launch_prefix(G, q, k_prefix, v_prefix, prefix_len, ws, (hipStream_t)stream));
 }
 
 hta_status hta_tree_partials(const hta_desc* desc, const void* q, const void* k_tree,
@@ -196,8 +204,15 @@ hta_status hta_tree_partials(const hta_desc* desc, const void* q, const void* k_
   HTA_TRY(check_ptrs({q, k_tree, v_tree, parent_idx, prefix_len}));
   HTA_TRY(check_ws(p, workspace, workspace_bytes));
   const Workspace ws = carve(workspace, p);
+  hipStream_t s = (hipStream_t)stream;
+  if (G.f32) {  // masks and status, then the tree partial from the parent chains
+    HTA_TRY(hip_status(hta::launch_tree_attn_masked(G, nullptr, nullptr, nullptr, parent_idx,
+                                                    prefix_len, ws, ws.masks, false, s)));
+    return hip_status(
+        hta::launch_tree_chain(G, q, k_tree, v_tree, parent_idx, prefix_len, ws, s));
+  }
   return hip_status(hta::launch_tree_attn_masked(G, q, k_tree, v_tree, parent_idx, prefix_len, ws,
-                                                 ws.masks, true, (hipStream_t)stream));
+                                                 ws.masks, true, s));
 }
 
 hta_status hta_merge(const hta_desc* desc, const int32_t* prefix_len, int32_t include_tree,

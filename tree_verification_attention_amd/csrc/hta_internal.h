@@ -34,6 +34,7 @@ struct Geometry {
   int32_t chunk;        // prefix keys per split
   int32_t S;            // number of prefix splits (the tree partial is slot S)
   float scale;          // softmax scale
+  int32_t f32;          // 1: q, k_*, v_* are fp32 (else bf16)
 };
 
 struct Workspace {
@@ -59,6 +60,16 @@ hipError_t launch_tree_merge(const Geometry& g, const void* q, const void* k_tre
                              const void* v_tree, const int32_t* parent_idx,
                              const int32_t* prefix_len, float* out, float* lse,
                              const Workspace& ws, hipStream_t stream);
+
+// The tree partial (slot S) computed from the parent chains, row by row (any input dtype);
+// status and masks are left to tree_attn_masked.
+hipError_t launch_tree_chain(const Geometry& g, const void* q, const void* k_tree,
+                             const void* v_tree, const int32_t* parent_idx,
+                             const int32_t* prefix_len, const Workspace& ws, hipStream_t stream);
+// The prefix pass for fp32 inputs (VALU, exact fp32 arithmetic; for small validation shapes).
+hipError_t launch_prefix_attn_f32(const Geometry& g, const void* q, const void* k_prefix,
+                                  const void* v_prefix, const int32_t* prefix_len,
+                                  const Workspace& ws, hipStream_t stream);
 
 // How the prefix pass blocks the query rows of one KV head: mt full row tiles per wave,
 // tiles_per_block row tiles per workgroup, blocks workgroups per (sequence, KV head, chunk).

@@ -42,14 +42,14 @@ constexpr int kMaxT = 256;
 struct MergeArgs {
   const int32_t* prefix_len;
   const int32_t* status;   // [B] or null: read by the plain merge
-  const float* lse_part;
-  const float* o_part;
+  float* lse_part;               // read by the merges, written by the tree-only form
+  float* o_part;
   float* out;
   float* lse;
   // fused merge only
-  const unsigned short* q;       // bf16 [B, T, Hq, D]
-  const unsigned short* k_tree;  // [B, Hkv, T, D]
-  const unsigned short* v_tree;
+  const void* q;                 // in_dtype [B, T, Hq, D]
+  const void* k_tree;            // [B, Hkv, T, D]
+  const void* v_tree;
   const int32_t* parent_idx;     // [B, T]
   int32_t* status_out;           // [B]
   Geometry g;
@@ -70,9 +70,14 @@ __device__ inline float group_sum4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__device__ inline float bf16_to_f32(unsigned short h) {
+__device__ inline float to_f32(unsigned short h) {  // bf16 bits, widened exactly
   return __builtin_bit_cast(float, (uint32_t)h << 16);
 }
+__device__ inline float to_f32(float x) { return x; }
+
+// What one launch does: the plain merge (tree partial read from slot S), the merge with the
+// tree part fused in, or the tree part alone written as the tree partial (slot S).
+enum Mode { kPlain = 0, kFused = 1, kTreeOnly = 2 };
 
 // sum over the 16 lanes of a part group
 __device__ inline float lane16_sum(float x) {
@@ -89,8 +94,11 @@ __device__ inline float group_max4(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-template <int D, bool FUSED>
+// TIN: element type of q, k_tree, v_tree (unsigned short = bf16 bits, or float)
+template <int D, int MODE, typename TIN>
 __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
+  constexpr bool FUSED = MODE != kPlain;   // computes the tree part
+  constexpr bool PREFIX = MODE != kTreeOnly;
   constexpr int DPL = D / 16;   // output dimensions per lane of a part group
   constexpr int NV = DPL / 4;   // float4 loads per part and lane
   constexpr int kBatch = 9;     // splits per lane per pass: 36 per pass
@@ -114,12 +122,12 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   const float* lrow = a.lse_part + base * G.R_pad + r;                 // slot s at s * R_pad
   const float* orow = a.o_part + (base * G.R_pad + r) * D + DPL * dl;  // slot s at s * R_pad * D
   const size_t ostride = (size_t)G.R_pad * D;
-  const bool tree_slot = !FUSED && a.include_tree;  // the plain merge's tree partial
+  const bool tree_slot = MODE == kPlain && a.include_tree;  // the plain merge's tree partial
 
   // ---- issue the loads
   const int Lb = a.prefix_len[b];
   const int st = (!FUSED && a.status) ? a.status[b] : 0;
-  const float lse_lane = lane < G.S ? lrow[(size_t)lane * G.R_pad] : -INFINITY;
+  const float lse_lane = (PREFIX && lane < G.S) ? lrow[(size_t)lane * G.R_pad] : -INFINITY;
   const float lse_tree = tree_slot ? lrow[(size_t)G.S * G.R_pad] : -INFINITY;
   float4 vt[NV];
 #pragma unroll
@@ -135,9 +143,9 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
       const int j = lane + 64 * k;
       par[k] = j < T ? a.parent_idx[(size_t)b * T + j] : -1;
     }
-    const unsigned short* qp = a.q + (size_t)row_id * D + DPL * dl;
+    const TIN* qp = (const TIN*)a.q + (size_t)row_id * D + DPL * dl;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) qv[e] = bf16_to_f32(qp[e]);
+    for (int e = 0; e < DPL; ++e) qv[e] = to_f32(qp[e]);
   }
   float lk[kBatch];
   float4 v[kBatch][NV];
@@ -147,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
     lk[k] = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NV; ++j) v[k][j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (p < G.S) {
+    if (PREFIX && p < G.S) {
       lk[k] = lrow[(size_t)p * G.R_pad];
 #pragma unroll
       for (int j = 0; j < NV; ++j) v[k][j] = ((const float4*)(orow + (size_t)p * ostride))[j];
@@ -170,9 +178,17 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
     }
     const bool tree_bad = __builtin_amdgcn_ballot_w64(bad_lane != 0) != 0;
     const bool len_bad = Lb < 0 || Lb > G.Lmax;
-    if (i == 0 && h == 0 && lane == 0)
+    if (MODE == kFused && i == 0 && h == 0 && lane == 0)
       a.status_out[b] = (tree_bad ? kStatusTree : 0) | (len_bad ? kStatusPrefixLen : 0);
-    bad = tree_bad || len_bad;
+    bad = MODE == kFused ? (tree_bad || len_bad) : tree_bad;
+  }
+  if (MODE == kTreeOnly && bad) {  // the tree partial of a rejected tree is NaN
+    float* tp = a.o_part + ((base + G.S) * G.R_pad + r) * D + DPL * dl;
+    if (pg == 0)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) tp[e] = NAN;
+    if (lane == 0) a.lse_part[(base + G.S) * G.R_pad + r] = NAN;
+    return;
   }
   if (bad) {
     if (pg == 0)
@@ -190,8 +206,8 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   if constexpr (FUSED) {
     __builtin_amdgcn_wave_barrier();  // s_par written by this wave is read below
     const float c = G.scale * kLog2e;
-    const unsigned short* Kt = a.k_tree + ((size_t)b * G.Hkv + kv) * (size_t)T * D + DPL * dl;
-    const unsigned short* Vt = a.v_tree + ((size_t)b * G.Hkv + kv) * (size_t)T * D + DPL * dl;
+    const TIN* Kt = (const TIN*)a.k_tree + ((size_t)b * G.Hkv + kv) * (size_t)T * D + DPL * dl;
+    const TIN* Vt = (const TIN*)a.v_tree + ((size_t)b * G.Hkv + kv) * (size_t)T * D + DPL * dl;
     // one batch of keys, one per part group (key < 0: none): score, then online softmax
     auto batch = [&](int my, const float (&kv8)[DPL], const float (&vv)[DPL]) {
       float sc = 0.f;
@@ -212,12 +228,12 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
 #pragma unroll
       for (int e = 0; e < DPL; ++e) kv8[e] = vv[e] = 0.f;
       if (my >= 0) {
-        const unsigned short* kp = Kt + (size_t)my * D;
-        const unsigned short* vp = Vt + (size_t)my * D;
+        const TIN* kp = Kt + (size_t)my * D;
+        const TIN* vp = Vt + (size_t)my * D;
 #pragma unroll
         for (int e = 0; e < DPL; ++e) {
-          kv8[e] = bf16_to_f32(kp[e]);
-          vv[e] = bf16_to_f32(vp[e]);
+          kv8[e] = to_f32(kp[e]);
+          vv[e] = to_f32(vp[e]);
         }
       }
     };
@@ -251,6 +267,19 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
       load_key(my, kk, vv);
       batch(my, kk, vv);
     }
+  }
+
+  if constexpr (MODE == kTreeOnly) {  // normalise and write the tree partial (slot S)
+    const float ltot = group_sum4(lt);
+    const float inv = 1.f / ltot;
+    float* tp = a.o_part + ((base + G.S) * G.R_pad + r) * D + DPL * dl;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      const float o = group_sum4(at[e]) * inv;
+      if (pg == 0) tp[e] = o;
+    }
+    if (lane == 0) a.lse_part[(base + G.S) * G.R_pad + r] = (mt + __log2f(ltot)) * kLn2;
+    return;
   }
 
   // ---- weights against the largest log-sum-exp (log2 units)
@@ -331,18 +360,40 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   if (lane == 0) *lsep = (M + __log2f(wsum)) * kLn2;
 }
 
-template <bool FUSED>
+template <int MODE, typename TIN>
 hipError_t launch_merge(const MergeArgs& a, const Geometry& g, hipStream_t stream) {
   const long nrows = (long)g.B * g.T * g.Hq;
   const int rows_per_block = kThreads / 64;
   dim3 grid((unsigned)((nrows + rows_per_block - 1) / rows_per_block));
   if (g.D == 128)
-    hipLaunchKernelGGL((lse_merge<128, FUSED>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((lse_merge<128, MODE, TIN>), grid, dim3(kThreads), 0, stream, a);
   else if (g.D == 64)
-    hipLaunchKernelGGL((lse_merge<64, FUSED>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((lse_merge<64, MODE, TIN>), grid, dim3(kThreads), 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_tree_mode(const Geometry& g, const void* q, const void* k_tree,
+                            const void* v_tree, const int32_t* parent_idx,
+                            const int32_t* prefix_len, float* out, float* lse,
+                            const Workspace& ws, hipStream_t stream) {
+  MergeArgs a = {};
+  a.prefix_len = prefix_len;
+  a.lse_part = ws.lse_part;
+  a.o_part = ws.o_part;
+  a.out = out;
+  a.lse = lse;
+  a.q = q;
+  a.k_tree = k_tree;
+  a.v_tree = v_tree;
+  a.parent_idx = parent_idx;
+  a.status_out = ws.status;
+  a.g = g;
+  a.include_tree = 1;
+  return g.f32 ? launch_merge<MODE, float>(a, g, stream)
+               : launch_merge<MODE, unsigned short>(a, g, stream);
 }
 
 }  // namespace
@@ -358,27 +409,23 @@ hipError_t launch_lse_merge(const Geometry& g, const int32_t* prefix_len, bool i
   a.lse = lse;
   a.g = g;
   a.include_tree = include_tree ? 1 : 0;
-  return launch_merge<false>(a, g, stream);
+  return launch_merge<kPlain, unsigned short>(a, g, stream);
 }
 
 hipError_t launch_tree_merge(const Geometry& g, const void* q, const void* k_tree,
                              const void* v_tree, const int32_t* parent_idx,
                              const int32_t* prefix_len, float* out, float* lse,
                              const Workspace& ws, hipStream_t stream) {
-  MergeArgs a = {};
-  a.prefix_len = prefix_len;
-  a.lse_part = ws.lse_part;
-  a.o_part = ws.o_part;
-  a.out = out;
-  a.lse = lse;
-  a.q = (const unsigned short*)q;
-  a.k_tree = (const unsigned short*)k_tree;
-  a.v_tree = (const unsigned short*)v_tree;
-  a.parent_idx = parent_idx;
-  a.status_out = ws.status;
-  a.g = g;
-  a.include_tree = 1;
-  return launch_merge<true>(a, g, stream);
+  return launch_tree_mode<kFused>(g, q, k_tree, v_tree, parent_idx, prefix_len, out, lse, ws,
+                                  stream);
+}
+
+hipError_t launch_tree_chain(const Geometry& g, const void* q, const void* k_tree,
+                             const void* v_tree, const int32_t* parent_idx,
+                             const int32_t* prefix_len, const Workspace& ws,
+                             hipStream_t stream) {
+  return launch_tree_mode<kTreeOnly>(g, q, k_tree, v_tree, parent_idx, prefix_len, nullptr,
+                                     nullptr, ws, stream);
 }
 
 }  // namespace hta
