@@ -23,15 +23,15 @@
 //    work of one wave overlaps the MFMAs of the other, so the second group runs one step
 //    behind the first: while one wave of a SIMD computes its softmax, the other feeds the
 //    matrix core.  Each wave holds MT row tiles.  Leftover tiles (when the count is not a
-//    multiple of 8) go to the second group, split by output dimensions: each of its waves
-//    forms the leftover scores and writes its own slice of d.  The first group instead
-//    streams the tiles and builds V^T, so both groups carry similar work per tile.
+//    multiple of 8) go to the first group, split by output dimensions: each of its waves
+//    forms the leftover scores and writes its own slice of d.  The first group also issues
+//    the tile loads; the second builds V^T, so both groups carry similar work per tile.
 //  * Memory: K and V tiles of 64 keys stream HBM -> LDS with direct LDS loads
 //    (global_load_lds_dwordx4, no register staging), two to three tiles in flight while
 //    one is consumed.  Rows land unpadded with an XOR swizzle of their 16-byte chunks so
 //    operand reads are bank-conflict-free.  Keys past the chunk end re-read the last valid
 //    key (never the padding) and are masked.
-//  * V^T operand: once per tile the first group turns the landed bf16 V tile into an fp16
+//  * V^T operand: once per tile the second group turns the landed bf16 V tile into an fp16
 //    V^T tile (transposing reads ds_read_b64_tr_b16, widening in registers, one 16-byte
 //    store per lane) laid out in the exact key order of the P^T operand, so the PV product
 //    reads plain conflict-free 16-byte operands.  This runs one tile ahead of the compute.
@@ -67,7 +67,7 @@ struct Layout {
   static constexpr int kRowBytes = D * 2;
   static constexpr int kChunks = D / 8;                             // 16-byte chunks per row
   static constexpr int kTileBytes = kKeyTile * kRowBytes;           // one K, V or V^T tile
-  // the first wave group (4 waves) streams the tiles and builds V^T
+  // the first wave group (4 waves) issues the tile loads
   static constexpr int kDmaPerWave = kTileBytes / (4 * 1024);  // per tensor per tile
   static constexpr int kKRing = 0;
   static constexpr int kVRing = kKStages * kTileBytes;
@@ -81,25 +81,8 @@ __device__ __forceinline__ int swz_vt(int d) { return (d >> 1) & 7; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)(p);
-}
-
-// Four transposing 64-bit LDS reads (ds_read_b64_tr_b16), completed before the block ends.
-// Written as one asm block with its own wait: the compiler treats the builtin as a possible
-// reader of the direct-load destinations and would otherwise drain every outstanding direct
-// load (vmcnt(0)) in front of it, which stalls the tile prefetch each iteration.  Callers
-// order these reads after the data landed (wait_and_barrier).
-__device__ __forceinline__ void tr_read_b64_x4(const unsigned char* const (&p)[4], i16x4 (&r)[4]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %4\n\t"
-      "ds_read_b64_tr_b16 %1, %5\n\t"
-      "ds_read_b64_tr_b16 %2, %6\n\t"
-      "ds_read_b64_tr_b16 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-      : "v"(lds_addr(p[0])), "v"(lds_addr(p[1])), "v"(lds_addr(p[2])), "v"(lds_addr(p[3]))
-      : "memory");
+__device__ __forceinline__ i16x4 tr_read_b64(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
 }
 
 __device__ __forceinline__ _Float16 bf16_bits_to_f16(short h) {
@@ -194,10 +177,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   auto full_tile = [&](int k) { return t0 + wg * (kWaves / 2) * MT + 4 * k + ww; };
   bf16x8 qop[MTA][DS];
 
-  // Leftover tiles (second wave group only): NL = 1 -> one tile shared by its 4 waves,
+  // Leftover tiles (first wave group only): NL = 1 -> one tile shared by its 4 waves,
   // NL = 2 -> tile ww/2 shared by 2 waves; each wave owns LDB output d-blocks from ldb0.
   constexpr int LDB = NL > 0 ? DB * NL / 4 : 1;
-  const bool has_left = LEFT && wg == 1;
+  const bool has_left = LEFT && wg == 0;
   const int ltile = t0 + kWaves * MT + (NL == 2 ? (ww >> 1) : 0);
   const int ldb0 = (NL == 2 ? (ww & 1) : ww) * LDB;
   bf16x8 qopl[DS];
@@ -218,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   auto transpose_v = [&](int t) {
     const unsigned char* vs = lds + Y::kVRing + (t % kVStages) * Y::kTileBytes;
     unsigned char* vt = lds + Y::kVt + (t % kVtStages) * Y::kTileBytes;
-    constexpr int kUnits = 2 * DB / 4;  // (d block, half) units per first-group wave
+    constexpr int kUnits = 2 * DB / 4;  // (d block, half) units per second-group wave
     static_assert(kUnits % 2 == 0, "units are read in pairs");
 #pragma unroll
     for (int i = 0; i < kUnits; i += 2) {
@@ -235,8 +218,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
         const int d = 16 * db + l16;
         dst[u] = d * (kKeyTile * 2) + 16 * ((4 * ks + grp) ^ swz_vt(d));
       }
+      // (the compiler drains this wave's direct loads before a transposing read; the second
+      // group issues none, so that wait is free here)
       i16x4 r[4];
-      tr_read_b64_x4(src, r);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) r[k] = tr_read_b64(src[k]);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         f16x8 h;
@@ -466,26 +452,30 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   // halves as X(t,0) Y(t,0) X(t,1) Y(t,1) (X: scores and softmax, Y: PV); the second wave
   // group runs one step behind the first (it finishes Y(t-1,1) at the start of tile t), so on
   // each SIMD one wave's softmax arithmetic overlaps the other's matrix products.  Only the
-  // second group carries leftover rows.
+  // first group carries leftover rows.
   auto run_chunk = [&](auto group) {
     constexpr bool LAG = decltype(group)::value;  // second wave group
-    constexpr std::integral_constant<bool, LAG && LEFT> tag{};
-    if constexpr (!LAG)
-      for (int t = 0; t < 3 && t < ntiles; ++t) issue(t);
-    // the query loads queue behind the first tiles (the compiler drains every vector-memory
-    // load before the first use of their registers, so issuing them first would serialise
-    // their latency with that of the tiles)
+    constexpr std::integral_constant<bool, !LAG && LEFT> tag{};
+    // Prologue: tile 0 and the query operands first, then tiles 1 and 2.  The compiler
+    // does not count direct loads, so it would wait for every one of them (vmcnt(0)) before
+    // the first use of the query registers; an explicit full wait placed before tiles 1
+    // and 2 are issued lets them stream while tile 0 is consumed.
+    if constexpr (!LAG) issue(0);
 #pragma unroll
     for (int k = 0; k < MT; ++k) load_q(full_tile(k), qop[k]);
     if constexpr (decltype(tag)::value) load_q(ltile, qopl);
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+    if constexpr (!LAG)
+      for (int t = 1; t < 3 && t < ntiles; ++t) issue(t);
     wait_tiles_and_barrier(min(2, ntiles - 1));
     set_reference(tag);
-    if constexpr (!LAG) transpose_v(0);
+    if constexpr (LAG) transpose_v(0);
     for (int t = 0; t < ntiles; ++t) {
       // tile t+1 landed (for the transpose), V^T of tile t complete, tile t-1 done
       wait_tiles_and_barrier(min(t + 2, ntiles - 1) - (t + 1));
       if constexpr (!LAG) {
         if (t + 3 < ntiles) issue(t + 3);  // refills the K stage of t-1 and the V stage of t
+      } else {
         if (t + 1 < ntiles) transpose_v(t + 1);
       }
       if constexpr (!LAG) {
