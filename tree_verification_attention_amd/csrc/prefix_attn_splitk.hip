@@ -37,10 +37,10 @@
 //    reads plain conflict-free 16-byte operands.  This runs one tile ahead of the compute.
 //  * Softmax in fp32 with exp2 (scale*log2(e) folded into one FMA) against a per-row
 //    reference: the maximum of the chunk's first 32 keys, raised only when a lane's
-//    probabilities of a 32-key half sum above 2^8 (a wave-wide ballot), so the accumulator
+//    probabilities of a 32-key half sum above 2^15 (a wave-wide ballot), so the accumulator
 //    rescale leaves the common path; the result is exact either way, since numerator and
 //    normaliser share the reference.  Probabilities enter the PV product as fp16
-//    (nearest-even, 11 significant bits, at most 2^8), V is widened from bf16 to fp16
+//    (nearest-even, 11 significant bits, at most 2^15), V is widened from bf16 to fp16
 //    (exact for |v| in [2^-14, 65504]), and the normaliser sums the unrounded fp32
 //    probabilities.
 #include "hta_internal.h"
@@ -60,7 +60,7 @@ constexpr int kVtStages = 3;  // V^T: tiles t-1 (second wave group), t (consumed
 // instruction classes of the scheduling hints (__builtin_amdgcn_sched_group_barrier masks)
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
-constexpr float kRaiseP = 256.f;  // probabilities stay below 2^8 (fp16 max 65504)
+constexpr float kRaiseP = 32768.f;  // probabilities stay below 2^15 (fp16 max 65504)
 
 template <int D>
 struct Layout {
@@ -263,7 +263,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   f16x8 popl;
   // Softmax reference per row (log2 units): starts at the maximum of the chunk's first 32
   // keys and is only raised when a lane's 8 probabilities of a half sum above kRaiseP, so
-  // p = 2^(s c - m_ref) < 2^8 always fits fp16 and the accumulator rescale is rare.
+  // p = 2^(s c - m_ref) <= 2^15 always fits fp16 and the accumulator rescale is rare (a
+  // lower bound raises the reference, and rescales, several times per chunk on peaky keys).
   float m_ref[MTA], m_refl = 0.f;
 
   // ---- scores S^T[key][row] of keys 32 h .. 32 h + 31 of tile t: this lane holds row l16,
@@ -367,7 +368,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
 #pragma unroll
     for (int k = 0; k < MT; ++k) need |= ls[k] > kRaiseP;
     if constexpr (WL) need |= lsl > kRaiseP;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+      // an empty volatile asm keeps this block a real (rarely taken) branch: without it the
+      // compiler executes the rescale unconditionally, which doubles the VALU work per step
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int k = 0; k < MT; ++k) {
         const float mx = group_max(ls[k]);
