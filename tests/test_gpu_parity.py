@@ -195,6 +195,22 @@ def test_verify_small_shapes(D, G):
     check_rows(w, out, lse)
 
 
+@pytest.mark.parametrize("G,T", [(4, 4), (8, 4), (4, 40), (2, 68), (4, 36), (4, 68), (1, 64),
+                                 (5, 50), (16, 17), (8, 40)])
+def test_verify_row_tilings(G, T):
+    """Row counts T*G covering every way the prefix pass splits query-row tiles over its
+    waves: 1 or 2 tiles only, leftover tiles of 1 and 2 (their keys split over waves),
+    several row blocks."""
+    gen = torch.Generator().manual_seed(300 + 7 * G + T)
+    par = [W.random_forest(T, gen), W.level_tree((T // 2, T - T // 2), gen)]
+    w = _small(f"tiles_G{G}_T{T}", par, B=2, Hq=2 * G, Hkv=2, D=128, L=777, plen=[777, 350],
+               seed=300 + G + T)
+    _log(f"verify row tilings G={G} T={T} rows={T * G}")
+    for chunk in (256, 0):
+        out, lse = run_gpu(w, chunk=chunk)
+        check_rows(w, out, lse, n_rows=3000)
+
+
 @pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 130, 256])
 def test_verify_tree_sizes(T):
     gen = torch.Generator().manual_seed(T)

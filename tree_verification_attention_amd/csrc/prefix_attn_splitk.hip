@@ -177,12 +177,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   auto full_tile = [&](int k) { return t0 + wg * (kWaves / 2) * MT + 4 * k + ww; };
   bf16x8 qop[MTA][DS];
 
-  // Leftover tiles (first wave group only): NL = 1 -> one tile shared by its 4 waves,
-  // NL = 2 -> tile ww/2 shared by 2 waves; each wave owns LDB output d-blocks from ldb0.
-  constexpr int LDB = NL > 0 ? DB * NL / 4 : 1;
+  // Leftover tiles (first wave group only), split by keys.  NL = 1: one tile; wave ww takes
+  // the 16-key block ww of every 64-key tile (half ww/2, block ww%2).  NL = 2: tile ww/2;
+  // wave ww takes the 32-key half ww%2.  Each wave keeps its own running softmax over its
+  // keys and accumulates all D output dimensions; the waves' partials are combined through
+  // LDS at the end.  The leftover products reuse the K and V^T operands the wave already
+  // reads for its own rows, and the leftover scores are never computed twice.
+  constexpr int LKB = NL == 2 ? 2 : 1;  // 16-key blocks per tile per wave
   const bool has_left = LEFT && wg == 0;
   const int ltile = t0 + kWaves * MT + (NL == 2 ? (ww >> 1) : 0);
-  const int ldb0 = (NL == 2 ? (ww & 1) : ww) * LDB;
+  const int lh = NL == 2 ? (ww & 1) : (ww >> 1);  // the wave's leftover half
+  const int ljj = NL == 2 ? 0 : (ww & 1);         // its first 16-key block in that half
   bf16x8 qopl[DS];
 
   // ---- stream K/V tiles into the LDS rings
@@ -246,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   };
 
   f32x4 acc[MTA][DB];
-  f32x4 accl[LDB];
+  f32x4 accl[LEFT ? DB : 1];
   float l_run[MTA], l_l = 0.f;
 #pragma unroll
   for (int k = 0; k < MT; ++k) {
@@ -255,12 +260,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     for (int db = 0; db < DB; ++db) acc[k][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
-  for (int j = 0; j < LDB; ++j) accl[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < (LEFT ? DB : 1); ++j) accl[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   // P^T operands of the half in flight: made by the softmax step, consumed by the PV step
   f16x8 pop[MTA];
-  f16x8 popl;
+  f16x8 popl;   // leftover P^T: NL = 2 (32 keys)
+  f16x4 popl4;  // leftover P^T: NL = 1 (16 keys)
   // Softmax reference per row (log2 units): starts at the maximum of the chunk's first 32
   // keys and is only raised when a lane's 8 probabilities of a half sum above kRaiseP, so
   // p = 2^(s c - m_ref) <= 2^15 always fits fp16 and the accumulator rescale is rare (a
@@ -292,20 +298,37 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
         for (int k = 0; k < MT; ++k)
           sc[k][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ds][j], qop[k][ds],
                                                              ds ? sc[k][j] : zero4, 0, 0, 0);
-        if constexpr (WL)
-          scl[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ds][j], qopl[ds], ds ? scl[j] : zero4,
-                                                           0, 0, 0);
       }
     }
     // instruction order: operand reads run two d-steps ahead of the products
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * (MT + (WL ? 1 : 0)), 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * MT, 0);
       if (ds + 2 < DS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (key0 + 32 * h + 32 > kend) {
+    // leftover scores of this wave's key blocks (the half's K operands are in registers):
+    // scl[i] holds keys 32 h + 16 (ljj + i) + 4 grp + r
+    if constexpr (WL) {
+      if (h == lh) {
+        if (NL == 2 || ljj == 0) {  // wave-uniform: no register array indexed at run time
+#pragma unroll
+          for (int i = 0; i < LKB; ++i) {
+            scl[i] = zero4;
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds)
+              scl[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ds][i], qopl[ds], scl[i], 0, 0, 0);
+          }
+        } else {
+          scl[0] = zero4;
+#pragma unroll
+          for (int ds = 0; ds < DS; ++ds)
+            scl[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ds][1], qopl[ds], scl[0], 0, 0, 0);
+        }
+      }
+    }
+    if (key0 + 32 * h + 32 > kend) {  // keys past the chunk end (last tile only)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -313,8 +336,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
           if (key0 + 32 * h + 16 * j + 4 * grp + r >= kend) {
 #pragma unroll
             for (int k = 0; k < MT; ++k) sc[k][j][r] = -INFINITY;
-            if constexpr (WL) scl[j][r] = -INFINITY;
           }
+      if constexpr (WL) {
+        if (h == lh) {
+#pragma unroll
+          for (int i = 0; i < LKB; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (key0 + 32 * h + 16 * (ljj + i) + 4 * grp + r >= kend) scl[i][r] = -INFINITY;
+        }
+      }
     }
   };
 
@@ -332,9 +363,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
       m_ref[k] = group_max(fmaxf(m0, m1) * a.c);
     }
     if constexpr (WL) {
-      const float m0 = fmaxf(fmaxf(scl[0][0], scl[0][1]), fmaxf(scl[0][2], scl[0][3]));
-      const float m1 = fmaxf(fmaxf(scl[1][0], scl[1][1]), fmaxf(scl[1][2], scl[1][3]));
-      m_refl = group_max(fmaxf(m0, m1) * a.c);
+      // the leftover reference: the maximum over this wave's first key block(s) of tile 0
+      if (lh != 0) scores(tag, 0, lh, sc, scl);
+      float m = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < LKB; ++i)
+        m = fmaxf(m, fmaxf(fmaxf(scl[i][0], scl[i][1]), fmaxf(scl[i][2], scl[i][3])));
+      m = group_max(m * a.c);
+      // a block wholly past the chunk end leaves no valid key: any finite reference will do
+      m_refl = m == -INFINITY ? 0.f : m;
     }
   };
 
@@ -346,20 +383,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     scores(tag, t, h, sc, scl);
     // ---- probabilities against the running reference (fp32)
     float p[MTA][8], pl[8], ls[MTA], lsl = 0.f;
+    // (sums as a tree: short dependency chains)
+    auto sum8 = [](const float (&v)[8]) {
+      return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    };
 #pragma unroll
     for (int k = 0; k < MT; ++k) {
-      ls[k] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < 8; ++e)
         p[k][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[k][e / 4][e % 4], a.c, -m_ref[k]));
-        ls[k] += p[k][e];
-      }
+      ls[k] = sum8(p[k]);
     }
+    const bool lhere = WL && h == lh;  // this step carries the wave's leftover keys
     if constexpr (WL) {
+      if (lhere) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pl[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(scl[e / 4][e % 4], a.c, -m_refl));
-        lsl += pl[e];
+        for (int e = 0; e < 4 * LKB; ++e)
+          pl[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(scl[e / 4][e % 4], a.c, -m_refl));
+        if constexpr (LKB == 2) lsl = sum8(pl);
+        else lsl = (pl[0] + pl[1]) + (pl[2] + pl[3]);
       }
     }
     // ---- raise the reference of rows whose probabilities outgrew kRaiseP (rare: the
@@ -367,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     bool need = false;
 #pragma unroll
     for (int k = 0; k < MT; ++k) need |= ls[k] > kRaiseP;
-    if constexpr (WL) need |= lsl > kRaiseP;
+    if constexpr (WL) need |= lhere && lsl > kRaiseP;
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
       // an empty volatile asm keeps this block a real (rarely taken) branch: without it the
       // compiler executes the rescale unconditionally, which doubles the VALU work per step
@@ -388,16 +430,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
         for (int db = 0; db < DB; ++db) acc[k][db] *= alpha;
       }
       if constexpr (WL) {
-        const float mx = group_max(lsl);
-        const float shift = mx > kRaiseP ? __log2f(mx) : 0.f;
-        const float alpha = __builtin_amdgcn_exp2f(-shift);
-        m_refl += shift;
-        l_l *= alpha;
-        lsl *= alpha;
+        if (lhere) {
+          const float mx = group_max(lsl);
+          const float shift = mx > kRaiseP ? __log2f(mx) : 0.f;
+          const float alpha = __builtin_amdgcn_exp2f(-shift);
+          m_refl += shift;
+          l_l *= alpha;
+          lsl *= alpha;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pl[e] *= alpha;
+          for (int e = 0; e < 4 * LKB; ++e) pl[e] *= alpha;
 #pragma unroll
-        for (int j = 0; j < LDB; ++j) accl[j] *= alpha;
+          for (int j = 0; j < DB; ++j) accl[j] *= alpha;
+        }
       }
     }
     // P^T operand of k-step h: element e <-> key 32 h + 16 (e / 4) + 4 grp + (e % 4)
@@ -408,9 +452,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
       l_run[k] += ls[k];
     }
     if constexpr (WL) {
+      if (lhere) {
+        if constexpr (LKB == 2) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) popl[e] = (_Float16)pl[e];
-      l_l += lsl;
+          for (int e = 0; e < 8; ++e) popl[e] = (_Float16)pl[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) popl4[e] = (_Float16)pl[e];
+        }
+        l_l += lsl;
+      }
     }
   };
 
@@ -438,14 +489,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
       if (db + 4 < DB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 1);
     }
     if constexpr (WL) {
-      // ldb0 is a runtime value: re-read these operands rather than index a register array
-      // with it (that would put the array in scratch memory)
+      // leftover rows: this wave's key block(s) of the half, all D dims, from the same V^T
+      // operands (a 16-key block is one 8-byte half of each operand: the K = 16 product)
+      if (h == lh) {
+        if constexpr (LKB == 2) {
 #pragma unroll
-      for (int j = 0; j < LDB; ++j) {
-        const int d = 16 * (ldb0 + j) + l16;
-        const f16x8 vl =
-            *(const f16x8*)(Vt + d * (kKeyTile * 2) + 16 * ((4 * h + grp) ^ swz_vt(d)));
-        accl[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, popl, accl[j], 0, 0, 0);
+          for (int db = 0; db < DB; ++db)
+            accl[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[db], popl, accl[db], 0, 0, 0);
+        } else if (ljj == 0) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            accl[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                __builtin_shufflevector(vop[db], vop[db], 0, 1, 2, 3), popl4, accl[db], 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            accl[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                __builtin_shufflevector(vop[db], vop[db], 4, 5, 6, 7), popl4, accl[db], 0, 0, 0);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -460,17 +521,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   auto run_chunk = [&](auto group) {
     constexpr bool LAG = decltype(group)::value;  // second wave group
     constexpr std::integral_constant<bool, !LAG && LEFT> tag{};
-    // Prologue: tile 0 and the query operands first, then tiles 1 and 2.  The compiler
-    // does not count direct loads, so it would wait for every one of them (vmcnt(0)) before
-    // the first use of the query registers; an explicit full wait placed before tiles 1
-    // and 2 are issued lets them stream while tile 0 is consumed.
-    if constexpr (!LAG) issue(0);
+    // Prologue: tiles 0 and 1 (the first iteration needs both) and the query operands, then
+    // tile 2.  The compiler does not count direct loads, so it would wait for every one of
+    // them (vmcnt(0)) before the first use of the query registers; an explicit full wait
+    // placed before tile 2 is issued lets it stream while tile 0 is consumed.
+    if constexpr (!LAG)
+      for (int t = 0; t < 2 && t < ntiles; ++t) issue(t);
 #pragma unroll
     for (int k = 0; k < MT; ++k) load_q(full_tile(k), qop[k]);
     if constexpr (decltype(tag)::value) load_q(ltile, qopl);
     __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
     if constexpr (!LAG)
-      for (int t = 1; t < 3 && t < ntiles; ++t) issue(t);
+      if (ntiles > 2) issue(2);
     wait_tiles_and_barrier(min(2, ntiles - 1));
     set_reference(tag);
     if constexpr (LAG) transpose_v(0);
@@ -516,16 +578,55 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     for (int db = 0; db < DB; ++db) *(f32x4*)(op + 16 * db) = acc[k][db] * inv;
     if (grp == 0) a.lse_part[slot * G.R_pad + row] = (m_ref[k] + __log2f(lt)) * kLn2;
   }
-  if (LEFT) {
-    // every sharer of a leftover tile holds the same m_l and l_l; each writes its d-blocks
-    const float lt = group_sum(l_l);
+  if constexpr (LEFT) {
+    // Leftover rows: combine the partials of the waves that share a leftover tile (each
+    // covered some of its keys) through LDS, as in the merge: M = max m_w, weights 2^(m_w-M).
+    // Every wave is past its loop (barrier), so the K ring is free.
+    constexpr int kStride = 4 * DB + 2;  // floats per (wave, lane): acc, then m and l
+    float* xl = (float*)(lds + Y::kKRing);
+    const float lsum = group_sum(l_l);
+    __syncthreads();
+    if (has_left) {
+      float* mine = xl + (ww * 64 + lane) * kStride;
+#pragma unroll
+      for (int j = 0; j < DB; ++j) *(f32x4*)(mine + 4 * j) = accl[j];
+      mine[4 * DB] = m_refl;
+      mine[4 * DB + 1] = lsum;
+    }
+    __syncthreads();
     if (has_left && ltile < t_end) {
+      // sharers: NL = 1 -> waves 0..3; NL = 2 -> waves 2 (ww/2) and 2 (ww/2) + 1.  This wave
+      // writes d-blocks [o0, o0 + DB * NL / 4) of the combined row.
+      constexpr int kShare = NL == 2 ? 2 : 4;
+      constexpr int kOwn = DB / kShare;
+      const int w0 = NL == 2 ? (ww & ~1) : 0;
+      const int o0 = (ww - w0) * kOwn;
+      float mw[kShare], lw[kShare], M = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kShare; ++i) {
+        const float* src = xl + ((w0 + i) * 64 + lane) * kStride;
+        mw[i] = src[4 * DB];
+        lw[i] = src[4 * DB + 1];
+        M = fmaxf(M, mw[i]);
+      }
+      float den = 0.f, wgt[kShare];
+#pragma unroll
+      for (int i = 0; i < kShare; ++i) {
+        wgt[i] = __builtin_amdgcn_exp2f(mw[i] - M);
+        den += wgt[i] * lw[i];
+      }
+      const float inv = 1.f / den;
       const int row = ltile * 16 + l16;
-      const float inv = 1.f / lt;
       float* op = a.o_part + (slot * G.R_pad + row) * D + 4 * grp;
 #pragma unroll
-      for (int j = 0; j < LDB; ++j) *(f32x4*)(op + 16 * (ldb0 + j)) = accl[j] * inv;
-      if (grp == 0 && ldb0 == 0) a.lse_part[slot * G.R_pad + row] = (m_refl + __log2f(lt)) * kLn2;
+      for (int j = 0; j < kOwn; ++j) {
+        f32x4 o = zero4;
+#pragma unroll
+        for (int i = 0; i < kShare; ++i)
+          o += wgt[i] * *(const f32x4*)(xl + ((w0 + i) * 64 + lane) * kStride + 4 * (o0 + j));
+        *(f32x4*)(op + 16 * (o0 + j)) = o * inv;
+      }
+      if (grp == 0 && o0 == 0) a.lse_part[slot * G.R_pad + row] = (M + __log2f(den)) * kLn2;
     }
   }
 }
