@@ -34,6 +34,16 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
 #endif
 }
 
+// A wave-uniform pointer made opaque to the optimiser, so that adding a per-lane 32-bit offset
+// to it stays "scalar base + vector offset" (the direct load's saddr form) instead of being
+// reassociated into a per-lane 64-bit address.
+__device__ __forceinline__ const unsigned char* opaque_uniform(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const unsigned char*)(((uint64_t)hi << 32) | lo);
+}
+
 // Direct loads of rows key0 .. key0+63 of a [rows, D] bf16 matrix into one K-swizzled and
 // one V-swizzled LDS tile, split over `nwaves` waves (wave index w).  Rows at or past `kend`
 // re-read row kend-1 (callers mask those keys).  Each wave issues 64 * D * 2 / (1024 * nwaves)
@@ -47,16 +57,36 @@ __device__ __forceinline__ void dma_kv_tile(const unsigned short* Kg, const unsi
   constexpr int kChunks = D / 8;                // 16-byte chunks per row
   constexpr int kTileBytes = kKeyTile * D * 2;
   constexpr int kPerWave = kTileBytes / (1024 * NWAVES);
+  constexpr int kBlkRows = 1024 / (2 * D);      // rows per 1 KB block
   static_assert(kPerWave * 1024 * NWAVES == kTileBytes, "tile splits into 1 KB blocks");
+  static_assert((NWAVES * kBlkRows) % 16 == 0, "a wave's blocks share one swizzle phase");
+  // The rows of this wave's blocks are NWAVES * kBlkRows apart, a multiple of both swizzle
+  // periods, so every block uses the same swizzled chunk: lane offsets are 32-bit values on
+  // a wave-uniform row base (scalar base + vector offset, no per-lane 64-bit addresses).
+  const int r0 = w * kBlkRows + lane / kChunks, p = lane % kChunks;
+  const uint32_t kx = 16u * (uint32_t)(p ^ swz_k<D>(r0));
+  const uint32_t vx = 16u * (uint32_t)(p ^ swz_v<D>(r0));
+  if (key0 + kKeyTile <= kend) {  // whole tile valid
+    const uint32_t ko = 2u * D * r0 + kx, vo = 2u * D * r0 + vx;
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+      const size_t row0 = (size_t)key0 + j * NWAVES * kBlkRows;
+      const int blk = j * NWAVES + w;
+      lds_dma16(opaque_uniform(Kg + row0 * D) + ko, ks + 1024 * blk);
+      lds_dma16(opaque_uniform(Vg + row0 * D) + vo, vs + 1024 * blk);
+    }
+    return;
+  }
+  const unsigned char* kb = opaque_uniform(Kg + (size_t)key0 * D);
+  const unsigned char* vb = opaque_uniform(Vg + (size_t)key0 * D);
+  const int last = kend - 1 - key0;  // >= 0: the tile holds at least one valid row
 #pragma unroll
   for (int j = 0; j < kPerWave; ++j) {
-    const int blk = j * NWAVES + w;   // 1 KB block of the tile written by this wave
-    if (SKIP_PAST_END && key0 + blk * (1024 / (2 * D)) >= kend) continue;
-    const int u = 64 * blk + lane;    // 16-byte chunk position within the tile
-    const int r = u / kChunks, p = u % kChunks;
-    const size_t gk = (size_t)min(key0 + r, kend - 1);
-    lds_dma16(Kg + gk * D + 8 * (p ^ swz_k<D>(r)), ks + 1024 * blk);
-    lds_dma16(Vg + gk * D + 8 * (p ^ swz_v<D>(r)), vs + 1024 * blk);
+    const int blk = j * NWAVES + w;  // 1 KB block of the tile written by this wave
+    if (SKIP_PAST_END && blk * kBlkRows > last) continue;
+    const uint32_t rr = (uint32_t)min(r0 + j * NWAVES * kBlkRows, last);
+    lds_dma16(kb + (2u * D * rr + kx), ks + 1024 * blk);
+    lds_dma16(vb + (2u * D * rr + vx), vs + 1024 * blk);
   }
 }
 

@@ -20,12 +20,12 @@
 //    between the products and its rescale factors are lane-local.
 //  * Two waves per SIMD (8 per workgroup), in two groups (waves 0-3 and 4-7, one of each
 //    per SIMD).  A wave's own VALU work overlaps its matrix-core work poorly, but the VALU
-//    work of one wave overlaps the MFMAs of the other, so the second group runs one step
-//    behind the first: while one wave of a SIMD computes its softmax, the other feeds the
-//    matrix core.  Each wave holds MT row tiles.  Leftover tiles (when the count is not a
-//    multiple of 8) go to the first group, split by output dimensions: each of its waves
-//    forms the leftover scores and writes its own slice of d.  The first group also issues
-//    the tile loads; the second builds V^T, so both groups carry similar work per tile.
+//    work of one wave overlaps the MFMAs of the other, so the two groups alternate between
+//    matrix-core phases and softmax phases half a phase pair apart (see run_chunk).  Each
+//    wave holds MT row tiles.  Leftover tiles (when the count is not a multiple of 8) go to
+//    the first group, split by keys: each of its waves covers some 16-key blocks of every
+//    tile for all D output dims, and the waves' partials are combined at the end.  The first
+//    group also issues the tile loads; the second builds V^T.
 //  * Memory: K and V tiles of 64 keys stream HBM -> LDS with direct LDS loads
 //    (global_load_lds_dwordx4, no register staging), two to three tiles in flight while
 //    one is consumed.  Rows land unpadded with an XOR swizzle of their 16-byte chunks so
@@ -56,7 +56,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kKStages = 4;  // K ring: tile t (scores), t+1 (landed), t+2, t+3 (in flight)
 constexpr int kVStages = 3;  // V ring: tile t+1 (being transposed), t+2, t+3 (in flight)
-constexpr int kVtStages = 3;  // V^T: tiles t-1 (second wave group), t (consumed), t+1 (made)
+constexpr int kVtStages = 3;  // V^T: tiles t-1 (PV of its last half), t, t+1 (being made)
 // instruction classes of the scheduling hints (__builtin_amdgcn_sched_group_barrier masks)
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
@@ -125,7 +125,7 @@ struct PrefixArgs {
 };
 
 // MT full row tiles per wave (both wave groups); NL leftover tiles (0..2) per block, split
-// over the second wave group by output d-blocks.
+// over the first wave group by keys.
 template <int D, int MT, int NL>
 __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) {
   using Y = Layout<D>;
@@ -375,12 +375,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     }
   };
 
-  // ---- step X(t, h): scores of keys 32 h .. 32 h + 31 of tile t, softmax, P^T operands
-  auto qk_softmax = [&](auto tag, int t, int h) {
+  // ---- softmax of the scores of half h (from scores()): probabilities, P^T operands
+  auto softmax = [&](auto tag, int h, f32x4 (&sc)[MTA][2], f32x4 (&scl)[2]) {
     constexpr bool WL = decltype(tag)::value;
-    f32x4 sc[MTA][2];
-    f32x4 scl[2];
-    scores(tag, t, h, sc, scl);
     // ---- probabilities against the running reference (fp32)
     float p[MTA][8], pl[8], ls[MTA], lsl = 0.f;
     // (sums as a tree: short dependency chains)
@@ -465,7 +462,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     }
   };
 
-  // ---- step Y(t, h): O^T[d][row] += V^T[d][key] P^T[key][row] for keys 32 h .. 32 h + 31
+  // ---- PV(t, h): O^T[d][row] += V^T[d][key] P^T[key][row] for keys 32 h .. 32 h + 31 of tile t
   auto pv = [&](auto tag, int t, int h) {
     constexpr bool WL = decltype(tag)::value;
     __builtin_amdgcn_sched_barrier(0);
@@ -513,11 +510,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   };
 
   // ---- pass over the chunk.  Tiles stream through the LDS rings: tile t+3 is issued while
-  // tile t is consumed and V of tile t+1 is transposed.  Each wave works through the 32-key
-  // halves as X(t,0) Y(t,0) X(t,1) Y(t,1) (X: scores and softmax, Y: PV); the second wave
-  // group runs one step behind the first (it finishes Y(t-1,1) at the start of tile t), so on
-  // each SIMD one wave's softmax arithmetic overlaps the other's matrix products.  Only the
-  // first group carries leftover rows.
+  // tile t is consumed and V of tile t+1 is transposed.  Per 32-key half a wave forms the
+  // scores (matrix core), the softmax (VALU) and the PV product (matrix core); merged with
+  // its neighbours this is an alternation of matrix-core phases (PV of one half + scores of
+  // the next) and VALU phases (softmax).  The second wave group runs half a phase pair
+  // behind the first -- it carries the scores of a tile's last half across the barrier and
+  // starts each tile with their softmax -- so on every SIMD one wave's softmax overlaps the
+  // other wave's products:
+  //   first group:   [PV(t-1,1) S(t,0)] [softmax(t,0)] [PV(t,0) S(t,1)] [softmax(t,1)]
+  //   second group:  [softmax(t-1,1)]   [PV(t-1,1) S(t,0)] [softmax(t,0)] [PV(t,0) S(t,1)]
+  // Only the first group carries leftover rows; the second also transposes V in its first
+  // VALU phase.
   auto run_chunk = [&](auto group) {
     constexpr bool LAG = decltype(group)::value;  // second wave group
     constexpr std::integral_constant<bool, !LAG && LEFT> tag{};
@@ -536,27 +539,26 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     wait_tiles_and_barrier(min(2, ntiles - 1));
     set_reference(tag);
     if constexpr (LAG) transpose_v(0);
+    f32x4 sc[MTA][2];  // scores of the half in flight (the second group carries them on)
+    f32x4 scl[2];
     for (int t = 0; t < ntiles; ++t) {
       // tile t+1 landed (for the transpose), V^T of tile t complete, tile t-1 done
       wait_tiles_and_barrier(min(t + 2, ntiles - 1) - (t + 1));
       if constexpr (!LAG) {
         if (t + 3 < ntiles) issue(t + 3);  // refills the K stage of t-1 and the V stage of t
       } else {
+        if (t > 0) softmax(tag, 1, sc, scl);
         if (t + 1 < ntiles) transpose_v(t + 1);
       }
-      if constexpr (!LAG) {
-        qk_softmax(tag, t, 0);
-        pv(tag, t, 0);
-        qk_softmax(tag, t, 1);
-        pv(tag, t, 1);
-      } else {
-        if (t > 0) pv(tag, t - 1, 1);
-        qk_softmax(tag, t, 0);
-        pv(tag, t, 0);
-        qk_softmax(tag, t, 1);
-      }
+      if (t > 0) pv(tag, t - 1, 1);
+      scores(tag, t, 0, sc, scl);
+      softmax(tag, 0, sc, scl);
+      pv(tag, t, 0);
+      scores(tag, t, 1, sc, scl);
+      if constexpr (!LAG) softmax(tag, 1, sc, scl);
     }
-    if constexpr (LAG) pv(tag, ntiles - 1, 1);
+    if constexpr (LAG) softmax(tag, 1, sc, scl);
+    pv(tag, ntiles - 1, 1);
   };
 
   // the two groups run separate copies of the loop (same barrier sequence), so each copy
