@@ -87,6 +87,72 @@ def load_traffic(workload: str):
     return rec.get("traffic_bytes_per_launch")
 
 
+def _counter_means(run_dir: str, kernel_substr: str, counter: str):
+    """Mean per-dispatch value of one rocprofv3 counter over the dispatches of one kernel."""
+    import csv
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                    vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} samples of {kernel_substr} under {run_dir}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize_counters(workload: str, fetch_dir: str, write_dir: str, fetch_copy_dir: str,
+                       write_copy_dir: str) -> str:
+    """HBM traffic of the prefix kernel per launch from four rocprofv3 --pmc runs.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the prefix kernel (--mode prefix-only) are
+    scaled by what the same counters read for the plain 256 MiB copy (--mode copy), so the
+    result is in bytes actually moved.  Written next to the other profiles, with the kernel
+    source hash: the bench reports the figure only while the kernel source is unchanged.
+    """
+    copy_bytes = 256 << 20
+    kern = "prefix_attn_splitk"
+    f_k, nf = _counter_means(fetch_dir, kern, "FETCH_SIZE")
+    w_k, nw = _counter_means(write_dir, kern, "WRITE_SIZE")
+    f_c, _ = _counter_means(fetch_copy_dir, "copyBuffer", "FETCH_SIZE")
+    w_c, _ = _counter_means(write_copy_dir, "copyBuffer", "WRITE_SIZE")
+    f_factor = copy_bytes / (f_c * 1024)
+    w_factor = copy_bytes / (w_c * 1024)
+    rd = f_k * 1024 * f_factor
+    wr = w_k * 1024 * w_factor
+    w = W.by_name(workload)
+    alg = alg_figures(w)["prefix_bytes"]
+    rec = {
+        "kernel": kern, "workload": workload, "kernel_sha256_16": kernel_source_hash(),
+        "fetch_size_kib_per_dispatch": round(f_k, 2), "write_size_kib_per_dispatch": round(w_k, 2),
+        "dispatches_sampled": {"fetch": nf, "write": nw},
+        "copy_calibration": {"bytes_copied": copy_bytes, "fetch_size_kib": round(f_c, 2),
+                             "write_size_kib": round(w_c, 2), "fetch_factor": round(f_factor, 4),
+                             "write_factor": round(w_factor, 4)},
+        "hbm_read_bytes_per_launch": int(rd), "hbm_write_bytes_per_launch": int(wr),
+        "traffic_bytes_per_launch": int(rd + wr), "alg_bytes_per_launch": alg,
+        "read_over_alg": round(rd / alg, 4),
+        "commands": [
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- "
+            "python3 bench.py --mode prefix-only --steps 10 --warmup 2",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- "
+            "python3 bench.py --mode prefix-only --steps 10 --warmup 2",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_copy_dir} -o run -- "
+            "python3 bench.py --mode copy --steps 5 --warmup 1",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_copy_dir} -o run -- "
+            "python3 bench.py --mode copy --steps 5 --warmup 1",
+            f"python3 bench.py --summarize-counters {fetch_dir} {write_dir} {fetch_copy_dir} "
+            f"{write_copy_dir}",
+        ],
+    }
+    out = os.path.join(PROFILE_DIR, f"prefix_attn_splitk_{workload}_traffic.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    return out
+
+
 def cpu_baseline(w: W.Workload, max_seconds: float = 12.0):
     """Time the oracle (single-threaded fp64 C) on a bounded row sample, scaled per step."""
     import oracle  # test infrastructure: only this baseline leg uses it
@@ -114,14 +180,23 @@ def cpu_baseline(w: W.Workload, max_seconds: float = 12.0):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=500,
+                    help="untimed steps first: the engine clock settles after a few hundred")
     ap.add_argument("--workload", default="llama3_8b_32k", choices=W.CONFIG_NAMES)
     ap.add_argument("--chunk", type=int, default=0, help="split-K chunk (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", default="bench", choices=["bench", "prefix-only", "copy"],
                     help="prefix-only / copy: launch only that kernel (for counter runs)")
+    ap.add_argument("--summarize-counters", nargs=4, metavar="DIR",
+                    help="write the prefix kernel's HBM traffic from four rocprofv3 --pmc "
+                         "output folders (FETCH_SIZE, WRITE_SIZE, then the same for --mode "
+                         "copy) into profiles/ and exit; needs no GPU")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        print(summarize_counters(args.workload, *args.summarize_counters))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this path runs on one GPU (the work shards by KV head with no "
@@ -198,10 +273,19 @@ def main() -> int:
     us_per_step = wall / args.steps * 1e6
     log(f"[bench] step: {us_per_step:.2f} us")
 
+    # the same steps timed with HIP events on the launch stream (GPU time only)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(args.steps):
+        step(k)
+    e1.record(stream)
+    e1.synchronize()
+    step_events_us = e0.elapsed_time(e1) / args.steps * 1e3
+    log(f"[bench] step (HIP events): {step_events_us:.2f} us")
+
     # ---- dominant kernel alone, HIP events on the launch stream
     for k in range(args.warmup):
         prefix_only(k)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for k in range(args.steps):
         prefix_only(k)
@@ -254,6 +338,7 @@ def main() -> int:
             "roofline_frac": round(max(fig["step_bytes"] / (HBM_PEAK_GBS * 1e9),
                                        fig["step_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12))
                                    / (us_per_step * 1e-6), 4),
+            "events_us": round(step_events_us, 3),
             "kernel_us": {"prefix_attn_splitk": round(prefix_us, 3),
                           "tree_attn_masked": round(tree_us, 3),
                           "lse_merge": round(merge_us, 3)},
