@@ -203,40 +203,57 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   const int vr = lane & 15;
   const int vrow = 4 * grp + (vr >> 2);
   const int vch = (vr & 3) >> 1, vhalf = 8 * (vr & 1);
+  // Byte offset of tile t's slot in a ring, as one wave-uniform value: the compiler would
+  // otherwise split the modulo into parts it adds to every lane address separately.
+  auto ring_slot = [&](int base, int t, int stages) -> uint32_t {
+    return __builtin_amdgcn_readfirstlane(base + (t % stages) * Y::kTileBytes);
+  };
+  // Lane offsets (loop-invariant).  Every swizzle below depends on the lane only, so the
+  // ring slot is the one per-tile term and the remaining terms are immediate offsets.
+  constexpr int kUnits = 2 * DB / 4;  // (d block, half) units per second-group wave
+  static_assert(kUnits % 2 == 0, "units are read in pairs");
+  uint32_t tr_src[kUnits];  // row r0 = 32 ks + vrow of unit i (row r0 + 16 is +16 rows)
+#pragma unroll
+  for (int i = 0; i < kUnits; ++i) {
+    const int pr = ww + 4 * i;
+    const int db = pr >> 1, ks = pr & 1;
+    const int r0 = 32 * ks + vrow;
+    tr_src[i] = r0 * Y::kRowBytes + 16 * ((2 * db + vch) ^ swz_v<D>(r0)) + vhalf;
+  }
+  // V^T row d = 16 db + l16: the chunk swizzle depends on l16 only
+  const uint32_t tr_dst = l16 * (kKeyTile * 2) + 16 * ((4 * (ww & 1) + grp) ^ swz_vt(l16));
+  // K operand rows 32 h + 16 j + l16 at chunk 4 ds + grp: the K swizzle has period 16 rows,
+  // so it depends on l16 only
+  uint32_t k_lane[DS];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds)
+    k_lane[ds] = l16 * Y::kRowBytes + 16 * ((4 * ds + grp) ^ swz_k<D>(l16));
+  // V^T operand rows d = 16 db + l16 at chunk 4 h + grp (swizzle of l16 only)
+  const uint32_t vt_lane[2] = {(uint32_t)(l16 * (kKeyTile * 2) + 16 * ((0 + grp) ^ swz_vt(l16))),
+                               (uint32_t)(l16 * (kKeyTile * 2) + 16 * ((4 + grp) ^ swz_vt(l16)))};
   auto transpose_v = [&](int t) {
-    const unsigned char* vs = lds + Y::kVRing + (t % kVStages) * Y::kTileBytes;
-    unsigned char* vt = lds + Y::kVt + (t % kVtStages) * Y::kTileBytes;
-    constexpr int kUnits = 2 * DB / 4;  // (d block, half) units per second-group wave
-    static_assert(kUnits % 2 == 0, "units are read in pairs");
+    const unsigned char* vs = lds + ring_slot(Y::kVRing, t, kVStages);
+    unsigned char* vt = lds + ring_slot(Y::kVt, t, kVtStages);
 #pragma unroll
     for (int i = 0; i < kUnits; i += 2) {
-      const unsigned char* src[4];
-      int dst[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int pr = ww + 4 * (i + u);
-        const int db = pr >> 1, ks = pr & 1;
-        const int r0 = 32 * ks + vrow, r1 = r0 + 16;
-        const int c = 2 * db + vch;
-        src[2 * u] = vs + r0 * Y::kRowBytes + 16 * (c ^ swz_v<D>(r0)) + vhalf;
-        src[2 * u + 1] = vs + r1 * Y::kRowBytes + 16 * (c ^ swz_v<D>(r1)) + vhalf;
-        const int d = 16 * db + l16;
-        dst[u] = d * (kKeyTile * 2) + 16 * ((4 * ks + grp) ^ swz_vt(d));
-      }
       // (the compiler drains this wave's direct loads before a transposing read; the second
       // group issues none, so that wait is free here)
       i16x4 r[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) r[k] = tr_read_b64(src[k]);
+      for (int u = 0; u < 2; ++u) {
+        r[2 * u] = tr_read_b64(vs + tr_src[i + u]);
+        r[2 * u + 1] = tr_read_b64(vs + tr_src[i + u] + 16 * Y::kRowBytes);
+      }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
+        const int db = (ww + 4 * (i + u)) >> 1;
         f16x8 h;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           h[e] = bf16_bits_to_f16(r[2 * u][e]);
           h[4 + e] = bf16_bits_to_f16(r[2 * u + 1][e]);
         }
-        *(f16x8*)(vt + dst[u]) = h;
+        *(f16x8*)(vt + tr_dst + db * 16 * (kKeyTile * 2)) = h;
       }
     }
   };
@@ -278,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   auto scores = [&](auto tag, int t, int h, f32x4 (&sc)[MTA][2], f32x4 (&scl)[2]) {
     constexpr bool WL = decltype(tag)::value;
     __builtin_amdgcn_sched_barrier(0);
-    const unsigned char* Ks = lds + Y::kKRing + (t % kKStages) * Y::kTileBytes;
+    const unsigned char* Ks = lds + ring_slot(Y::kKRing, t, kKStages);
     const int key0 = kbeg + t * kKeyTile;
     // all K operands of the half are read up front, so the products start as soon as the
     // first ones land and the rest of the reads overlap them
@@ -286,10 +303,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = 32 * h + 16 * j + l16;
-        kop[ds][j] = *(const bf16x8*)(Ks + row * Y::kRowBytes + 16 * ((4 * ds + grp) ^ swz_k<D>(row)));
-      }
+      for (int j = 0; j < 2; ++j)
+        kop[ds][j] = *(const bf16x8*)(Ks + k_lane[ds] + (32 * h + 16 * j) * Y::kRowBytes);
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
 #pragma unroll
@@ -466,13 +481,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   auto pv = [&](auto tag, int t, int h) {
     constexpr bool WL = decltype(tag)::value;
     __builtin_amdgcn_sched_barrier(0);
-    const unsigned char* Vt = lds + Y::kVt + (t % kVtStages) * Y::kTileBytes;
+    const unsigned char* Vt = lds + ring_slot(Y::kVt, t, kVtStages) + vt_lane[h];
     f16x8 vop[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d = 16 * db + l16;
-      vop[db] = *(const f16x8*)(Vt + d * (kKeyTile * 2) + 16 * ((4 * h + grp) ^ swz_vt(d)));
-    }
+    for (int db = 0; db < DB; ++db) vop[db] = *(const f16x8*)(Vt + db * 16 * (kKeyTile * 2));
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
