@@ -154,7 +154,13 @@ def summarize_counters(workload: str, fetch_dir: str, write_dir: str, fetch_copy
 
 
 def cpu_baseline(w: W.Workload, max_seconds: float = 12.0):
-    """Time the oracle (single-threaded fp64 C) on a bounded row sample, scaled per step."""
+    """Time the oracle (plain fp64 C, one row per call of its loop nest) on a bounded sample of
+    the workload's query rows, scaled per step: once on one thread, then with the same rows
+    spread over the host's cores (the identical single-threaded code per row; the outputs
+    must be bitwise equal)."""
+    import concurrent.futures as cf
+    import platform
+
     import oracle  # test infrastructure: only this baseline leg uses it
     a = w.as_numpy()
     B, T, Hq = w.batch, w.tree_size, w.num_q_heads
@@ -169,12 +175,62 @@ def cpu_baseline(w: W.Workload, max_seconds: float = 12.0):
     ids = np.sort(rng.choice(total, size=n, replace=False))
     b, i, h = ids // (T * Hq), (ids // Hq) % T, ids % Hq
     t0 = time.perf_counter()
-    oracle.rows(a, w.scale, b, h, i)
-    dt = time.perf_counter() - t0
-    us_per_step = dt / n * total * 1e6
-    return {"value": us_per_step, "unit": "µs/step", "cores": 1, "kind": "oracle",
-            "sample": f"{n} of {total} query rows (b, head, node) of the same workload, "
-                      f"single-threaded fp64 C oracle, {dt:.1f} s, scaled to the full step"}
+    o1, l1 = oracle.rows(a, w.scale, b, h, i)
+    dt1 = time.perf_counter() - t0
+    threads = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+                         else (os.cpu_count() or 1)))
+    parts = np.array_split(np.arange(n), threads)
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(threads) as ex:  # the C call releases the GIL
+        res = list(ex.map(lambda ix: oracle.rows(a, w.scale, b[ix], h[ix], i[ix]), parts))
+    dtn = time.perf_counter() - t0
+    on = np.concatenate([r[0] for r in res])
+    ln = np.concatenate([r[1] for r in res])
+    cpu = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(x.split(":", 1)[1].strip() for x in f if x.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    return {"value": dtn / n * total * 1e6, "unit": "µs/step", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {total} query rows (b, head, node) of the same workload, fp64 C "
+                      f"oracle, rows spread over {threads} threads ({dtn:.1f} s), scaled to the "
+                      f"full step",
+            "single_thread_value": dt1 / n * total * 1e6,
+            "bitwise_equal_across_threads": bool(np.array_equal(o1, on) and np.array_equal(l1, ln)),
+            "cpu_model": cpu}
+
+
+def measured_peaks(dev) -> dict:
+    """What this GPU sustains right now: a 512 MiB device copy (HBM read + write) and a large
+    bf16 GEMM (the vendor BLAS, matrix cores).  Context for the spec peaks."""
+    n = 512 << 20
+    src = torch.empty(n // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    e1.synchronize()
+    copy_gbs = 2 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    x = torch.randn(m, m, device=dev).to(torch.bfloat16)
+    y = torch.randn(m, m, device=dev).to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(x, y)
+    e0.record()
+    for _ in range(10):
+        torch.matmul(x, y)
+    e1.record()
+    e1.synchronize()
+    gemm_tf = 2 * m ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del x, y
+    return {"hbm_copy_GBps": round(copy_gbs, 1), "bf16_gemm_TFLOPs": round(gemm_tf, 1),
+            "how": "512 MiB device copy (bytes read + written); 8192^3 bf16 torch.matmul"}
 
 
 def main() -> int:
@@ -282,6 +338,18 @@ def main() -> int:
     e1.synchronize()
     step_events_us = e0.elapsed_time(e1) / args.steps * 1e3
     log(f"[bench] step (HIP events): {step_events_us:.2f} us")
+    # each call between its own event pair: the spread of single steps
+    n_calls = min(args.steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_calls)]
+    for k, (a0, a1) in enumerate(evs):
+        a0.record(stream)
+        step(k)
+        a1.record(stream)
+    torch.cuda.synchronize()
+    per_call = np.array([a0.elapsed_time(a1) * 1e3 for a0, a1 in evs])
+    p10, p50, p90 = (float(np.percentile(per_call, q)) for q in (10, 50, 90))
+    log(f"[bench] single steps: p10 {p10:.2f} p50 {p50:.2f} p90 {p90:.2f} us")
 
     # ---- dominant kernel alone, HIP events on the launch stream
     for k in range(args.warmup):
@@ -339,6 +407,8 @@ def main() -> int:
                                        fig["step_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12))
                                    / (us_per_step * 1e-6), 4),
             "events_us": round(step_events_us, 3),
+            "per_call_us": {"p10": round(p10, 3), "p50": round(p50, 3), "p90": round(p90, 3),
+                            "calls": n_calls},
             "kernel_us": {"prefix_attn_splitk": round(prefix_us, 3),
                           "tree_attn_masked": round(tree_us, 3),
                           "lse_merge": round(merge_us, 3)},
@@ -357,6 +427,12 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": round(achieved_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
         },
     }
+    peaks = measured_peaks(dev)
+    log(f"[bench] measured peaks: {peaks}")
+    result["measured_peaks"] = peaks
+    result["roofline"]["frac_of_measured_peak"] = round(achieved_gbs / peaks["hbm_copy_GBps"], 4)
+    result["roofline"]["mfma"]["frac_of_measured_peak"] = round(
+        achieved_tflops / peaks["bf16_gemm_TFLOPs"], 4)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w)

@@ -580,26 +580,44 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
 
   // ---- normalise and write this chunk's partial
   const size_t slot = ((size_t)b * G.Hkv + kv) * (G.S + 1) + s;
+  // A lane holds 4 consecutive dims of one row per d block, so direct stores would write
+  // 64-byte pieces of 16 rows per instruction.  Each wave stages its normalised rows in LDS
+  // (the V and V^T rings are free once every wave is past its loop) and writes them back
+  // whole: every store instruction covers 1 KB of consecutive rows.
+  __syncthreads();
+  {
+    constexpr int kC = D / 4;                        // 16-byte chunks per fp32 row
+    constexpr int kRowsPerInst = 64 * 16 / (D * 4);  // rows per 1 KB store instruction
+    static_assert(Y::kVRing + kWaves * 16 * D * 4 <= Y::kBytes, "staging fits the V rings");
+    unsigned char* stage = lds + Y::kVRing + wave * (16 * D * 4);
 #pragma unroll
-  for (int k = 0; k < MT; ++k) {
-    const int tile = full_tile(k);
-    const float lt = group_sum(l_run[k]);
-    if (tile >= t_end) continue;
-    const int row = tile * 16 + l16;
-    const float inv = 1.f / lt;
-    float* op = a.o_part + (slot * G.R_pad + row) * D + 4 * grp;
+    for (int k = 0; k < MT; ++k) {
+      const int tile = full_tile(k);
+      const float lt = group_sum(l_run[k]);
+      if (tile >= t_end) continue;
+      const float inv = 1.f / lt;
+      // chunk c of row r sits at chunk position c ^ r (conflict-free both ways)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) *(f32x4*)(op + 16 * db) = acc[k][db] * inv;
-    if (grp == 0) a.lse_part[slot * G.R_pad + row] = (m_ref[k] + __log2f(lt)) * kLn2;
+      for (int db = 0; db < DB; ++db)
+        *(f32x4*)(stage + l16 * D * 4 + 16 * ((4 * db + grp) ^ (l16 & (kC - 1)))) =
+            acc[k][db] * inv;
+      // (the same wave reads the staging back: its LDS accesses complete in order)
+#pragma unroll
+      for (int j = 0; j < 16 / kRowsPerInst; ++j) {
+        const int rr = j * kRowsPerInst + lane / kC, c = lane % kC;
+        const f32x4 v = *(const f32x4*)(stage + rr * D * 4 + 16 * (c ^ (rr & (kC - 1))));
+        *(f32x4*)(a.o_part + (slot * G.R_pad + tile * 16 + rr) * D + 4 * c) = v;
+      }
+      if (grp == 0) a.lse_part[slot * G.R_pad + tile * 16 + l16] = (m_ref[k] + __log2f(lt)) * kLn2;
+    }
   }
   if constexpr (LEFT) {
     // Leftover rows: combine the partials of the waves that share a leftover tile (each
     // covered some of its keys) through LDS, as in the merge: M = max m_w, weights 2^(m_w-M).
-    // Every wave is past its loop (barrier), so the K ring is free.
+    // Every wave is past its loop (barrier above), so the K ring is free.
     constexpr int kStride = 4 * DB + 2;  // floats per (wave, lane): acc, then m and l
     float* xl = (float*)(lds + Y::kKRing);
     const float lsum = group_sum(l_l);
-    __syncthreads();
     if (has_left) {
       float* mine = xl + (ww * 64 + lane) * kStride;
 #pragma unroll
