@@ -41,7 +41,7 @@ constexpr int kMaxT = 256;
 
 struct MergeArgs {
   const int32_t* prefix_len;
-  const int32_t* status;   // [B] or null: read by the plain merge
+  const int32_t* status;   // [B]: read by the plain merge (the tree pass status)
   float* lse_part;               // read by the merges, written by the tree-only form
   float* o_part;
   float* out;
@@ -126,22 +126,27 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
 
   // ---- issue the loads
   const int Lb = a.prefix_len[b];
-  const int st = (!FUSED && a.status) ? a.status[b] : 0;
-  const float lse_lane = (PREFIX && lane < G.S) ? lrow[(size_t)lane * G.R_pad] : -INFINITY;
-  const float lse_tree = tree_slot ? lrow[(size_t)G.S * G.R_pad] : -INFINITY;
-  float4 vt[NV];
+  const int st = FUSED ? 0 : a.status[b];  // (read only where the tree slot is used)
+  // Loads are unconditional (indices clamped into range, the value replaced where it is
+  // used): a load under a lane-dependent branch makes the compiler wait for it inside the
+  // branch, which would serialise the loads instead of having them all in flight.
+  const float lse_raw = PREFIX ? lrow[(size_t)min(lane, G.S - 1) * G.R_pad] : 0.f;
+  const float lse_lane = (PREFIX && lane < G.S) ? lse_raw : -INFINITY;
+  float4 vt[NV];  // the plain merge's tree partial (slot S, always allocated)
+  const float lse_tree_raw = FUSED ? 0.f : lrow[(size_t)G.S * G.R_pad];
 #pragma unroll
-  for (int j = 0; j < NV; ++j) vt[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (tree_slot && pg == 0)
-#pragma unroll
-    for (int j = 0; j < NV; ++j) vt[j] = ((const float4*)(orow + (size_t)G.S * ostride))[j];
+  for (int j = 0; j < NV; ++j)
+    vt[j] = FUSED ? make_float4(0.f, 0.f, 0.f, 0.f)
+                  : ((const float4*)(orow + (size_t)G.S * ostride))[j];
+  const float lse_tree = tree_slot ? lse_tree_raw : -INFINITY;
   int par[kMaxT / 64];
   float qv[DPL];
   if constexpr (FUSED) {
 #pragma unroll
     for (int k = 0; k < kMaxT / 64; ++k) {
       const int j = lane + 64 * k;
-      par[k] = j < T ? a.parent_idx[(size_t)b * T + j] : -1;
+      const int pj = a.parent_idx[(size_t)b * T + min(j, T - 1)];
+      par[k] = j < T ? pj : -1;
     }
     const TIN* qp = (const TIN*)a.q + (size_t)row_id * D + DPL * dl;
 #pragma unroll
@@ -149,21 +154,30 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   }
   float lk[kBatch];
   float4 v[kBatch][NV];
+  auto load_parts = [&](int k0, int k1) {
 #pragma unroll
-  for (int k = 0; k < kBatch; ++k) {
-    const int p = pg + 4 * k;
-    lk[k] = -INFINITY;
+    for (int k = k0; k < k1; ++k) {
+      // slot pg + 4k, clamped: lanes past the last split re-read it and never use it
+      const int p = min(pg + 4 * k, G.S - 1);
+      lk[k] = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) v[k][j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (PREFIX && p < G.S) {
-      lk[k] = lrow[(size_t)p * G.R_pad];
+      for (int j = 0; j < NV; ++j) v[k][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (PREFIX && 4 * k < G.S) {  // wave-uniform
+        lk[k] = lrow[(size_t)p * G.R_pad];
 #pragma unroll
-      for (int j = 0; j < NV; ++j) v[k][j] = ((const float4*)(orow + (size_t)p * ostride))[j];
+        for (int j = 0; j < NV; ++j) v[k][j] = ((const float4*)(orow + (size_t)p * ostride))[j];
+      }
     }
-  }
+  };
+  // A wave's loads complete in order.  The fused merge issues the first partials, then the
+  // tree rows its row needs (found from the parent pointers, which were issued first), then
+  // the remaining partials: the tree part is computed while those are still arriving.
+  constexpr int kEarly = FUSED ? 4 : kBatch;
+  load_parts(0, kEarly);
 
   // ---- validate
-  bool bad = Lb < 0 || Lb > G.Lmax || st != 0;
+  bool bad = Lb < 0 || Lb > G.Lmax || (tree_slot && st != 0);
+  bool tree_bad = false;  // the chain walk needs only this verdict, not the prefix length
   if constexpr (FUSED) {
     // parent pointers: parent[j] in [-1, j-1] for every node (the tree is topologically
     // ordered); the verdict is wave-uniform
@@ -176,71 +190,53 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
         s_par[wave][j] = par[k];
       }
     }
-    const bool tree_bad = __builtin_amdgcn_ballot_w64(bad_lane != 0) != 0;
-    const bool len_bad = Lb < 0 || Lb > G.Lmax;
-    if (MODE == kFused && i == 0 && h == 0 && lane == 0)
-      a.status_out[b] = (tree_bad ? kStatusTree : 0) | (len_bad ? kStatusPrefixLen : 0);
-    bad = MODE == kFused ? (tree_bad || len_bad) : tree_bad;
+    tree_bad = __builtin_amdgcn_ballot_w64(bad_lane != 0) != 0;
+    bad = MODE == kFused ? (bad || tree_bad) : tree_bad;
   }
-  if (MODE == kTreeOnly && bad) {  // the tree partial of a rejected tree is NaN
-    float* tp = a.o_part + ((base + G.S) * G.R_pad + r) * D + DPL * dl;
-    if (pg == 0)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) tp[e] = NAN;
-    if (lane == 0) a.lse_part[(base + G.S) * G.R_pad + r] = NAN;
-    return;
-  }
-  if (bad) {
-    if (pg == 0)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) outp[e] = NAN;
-    if (lane == 0) *lsep = NAN;
-    return;
-  }
+  // (a rejected sequence is only acted on at the end: an early exit here would let the
+  // compiler wait for the verdict's loads before issuing the partial loads)
 
   // ---- fused: the tree part over the visible keys i, parent(i), ... (log2 units)
   float mt = -INFINITY, lt = 0.f;  // running maximum, this group's weight sum
   float at[DPL];                   // this group's weighted value sum
 #pragma unroll
   for (int e = 0; e < DPL; ++e) at[e] = 0.f;
+  const float c = G.scale * kLog2e;
+  const TIN* Kt = (const TIN*)a.k_tree + ((size_t)b * G.Hkv + kv) * (size_t)T * D + DPL * dl;
+  const TIN* Vt = (const TIN*)a.v_tree + ((size_t)b * G.Hkv + kv) * (size_t)T * D + DPL * dl;
+  // one batch of keys, one per part group (key < 0: none): score, then online softmax
+  auto batch = [&](int my, const float (&kv8)[DPL], const float (&vv)[DPL]) {
+    float sc = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) sc += qv[e] * kv8[e];
+    sc = lane16_sum(sc) * c;
+    if (my < 0) sc = -INFINITY;
+    // finite: the first batch holds the row's own node; later ones start at a valid key
+    const float m_new = fmaxf(mt, group_max4(sc));
+    const float alpha = __builtin_amdgcn_exp2f(mt - m_new);
+    const float p = __builtin_amdgcn_exp2f(sc - m_new);
+    mt = m_new;
+    lt = lt * alpha + p;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) at[e] = at[e] * alpha + p * vv[e];
+  };
+  // (no key: node 0 is read and its score masked, so its p is 0)
+  auto load_key = [&](int my, float (&kv8)[DPL], float (&vv)[DPL]) {
+    const TIN* kp = Kt + (size_t)max(my, 0) * D;
+    const TIN* vp = Vt + (size_t)max(my, 0) * D;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      kv8[e] = to_f32(kp[e]);
+      vv[e] = to_f32(vp[e]);
+    }
+  };
+  // the first eight keys of the chain (enough for trees up to depth 7) are found first and
+  // their K/V rows loaded together
+  int t = tree_bad ? -1 : i;  // next ancestor (wave-uniform); a chain ends at a root (-1)
+  int my0 = -1, my1 = -1;
+  float k0[DPL], v0[DPL], k1[DPL], v1[DPL];
   if constexpr (FUSED) {
     __builtin_amdgcn_wave_barrier();  // s_par written by this wave is read below
-    const float c = G.scale * kLog2e;
-    const TIN* Kt = (const TIN*)a.k_tree + ((size_t)b * G.Hkv + kv) * (size_t)T * D + DPL * dl;
-    const TIN* Vt = (const TIN*)a.v_tree + ((size_t)b * G.Hkv + kv) * (size_t)T * D + DPL * dl;
-    // one batch of keys, one per part group (key < 0: none): score, then online softmax
-    auto batch = [&](int my, const float (&kv8)[DPL], const float (&vv)[DPL]) {
-      float sc = 0.f;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) sc += qv[e] * kv8[e];
-      sc = lane16_sum(sc) * c;
-      if (my < 0) sc = -INFINITY;
-      // finite: the first batch holds the row's own node; later ones start at a valid key
-      const float m_new = fmaxf(mt, group_max4(sc));
-      const float alpha = __builtin_amdgcn_exp2f(mt - m_new);
-      const float p = __builtin_amdgcn_exp2f(sc - m_new);
-      mt = m_new;
-      lt = lt * alpha + p;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) at[e] = at[e] * alpha + p * vv[e];
-    };
-    auto load_key = [&](int my, float (&kv8)[DPL], float (&vv)[DPL]) {
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) kv8[e] = vv[e] = 0.f;
-      if (my >= 0) {
-        const TIN* kp = Kt + (size_t)my * D;
-        const TIN* vp = Vt + (size_t)my * D;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) {
-          kv8[e] = to_f32(kp[e]);
-          vv[e] = to_f32(vp[e]);
-        }
-      }
-    };
-    // the first eight keys of the chain (enough for trees up to depth 7) are found first and
-    // their K/V rows loaded together: one memory round trip
-    int t = i;  // next ancestor (wave-uniform); the chain ends at a root (parent -1)
-    int my0 = -1, my1 = -1;
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       if (pg == (g & 3)) {
@@ -249,13 +245,17 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
       }
       if (t >= 0) t = __builtin_amdgcn_readfirstlane(s_par[wave][t]);
     }
-    {
-      float k0[DPL], v0[DPL], k1[DPL], v1[DPL];
-      load_key(my0, k0, v0);
-      load_key(my1, k1, v1);
-      batch(my0, k0, v0);
-      if (__builtin_amdgcn_ballot_w64(my1 >= 0) != 0) batch(my1, k1, v1);  // wave-uniform
-    }
+    load_key(my0, k0, v0);
+    load_key(my1, k1, v1);
+  }
+  load_parts(kEarly, kBatch);
+  if (MODE == kFused && i == 0 && h == 0 && lane == 0) {  // the sequence's device status
+    const bool len_bad = Lb < 0 || Lb > G.Lmax;
+    a.status_out[b] = (tree_bad ? kStatusTree : 0) | (len_bad ? kStatusPrefixLen : 0);
+  }
+  if constexpr (FUSED) {
+    if (!tree_bad) batch(my0, k0, v0);
+    if (__builtin_amdgcn_ballot_w64(my1 >= 0) != 0) batch(my1, k1, v1);  // wave-uniform
     while (t >= 0) {  // deeper chains, four keys at a time
       int my = -1;
 #pragma unroll
@@ -270,29 +270,41 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   }
 
   if constexpr (MODE == kTreeOnly) {  // normalise and write the tree partial (slot S)
+    // (the tree partial of a rejected tree is NaN)
     const float ltot = group_sum4(lt);
     const float inv = 1.f / ltot;
     float* tp = a.o_part + ((base + G.S) * G.R_pad + r) * D + DPL * dl;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
       const float o = group_sum4(at[e]) * inv;
-      if (pg == 0) tp[e] = o;
+      if (pg == 0) tp[e] = bad ? NAN : o;
     }
-    if (lane == 0) a.lse_part[(base + G.S) * G.R_pad + r] = (mt + __log2f(ltot)) * kLn2;
+    if (lane == 0)
+      a.lse_part[(base + G.S) * G.R_pad + r] = bad ? NAN : (mt + __log2f(ltot)) * kLn2;
+    return;
+  }
+  if (bad) {  // a rejected sequence: NaN
+    if (pg == 0)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) outp[e] = NAN;
+    if (lane == 0) *lsep = NAN;
     return;
   }
 
-  // ---- weights against the largest log-sum-exp (log2 units)
-  const int nsplit = (Lb + G.chunk - 1) / G.chunk;  // non-empty prefix splits
-  float M = fmaxf(lane < nsplit ? lse_lane * kLog2e : -INFINITY, lse_tree * kLog2e);
-  for (int p = 64 + lane; p < nsplit; p += 64) M = fmaxf(M, lrow[(size_t)p * G.R_pad] * kLog2e);
-  M = wave_max(M);
+  // ---- weights against the largest log-sum-exp.  The maximum Mn is taken on the stored
+  // (natural-log) values and each weight is 2^((l - Mn) log2(e)): nothing is computed from a
+  // partial before the maximum, so the compiler has no reason to wait for one early.
+  const int nsplit = (Lb + G.chunk - 1) / G.chunk;  // non-empty prefix splits (Lb valid here)
+  float Mn = fmaxf(lane < nsplit ? lse_lane : -INFINITY, lse_tree);
+  for (int p = 64 + lane; p < nsplit; p += 64) Mn = fmaxf(Mn, lrow[(size_t)p * G.R_pad]);
+  Mn = wave_max(Mn);
   float ltot = 0.f;
   if constexpr (FUSED) {
-    ltot = group_sum4(lt);                 // the tree's weight sum relative to mt
-    M = fmaxf(M, mt + __log2f(ltot));      // the tree part's log-sum-exp
+    ltot = group_sum4(lt);                         // the tree's weight sum relative to mt
+    Mn = fmaxf(Mn, (mt + __log2f(ltot)) * kLn2);  // the tree part's log-sum-exp
   }
-  if (M == -INFINITY) {  // no visible key at all (prefix-only merge of an empty prefix)
+  const float M = Mn * kLog2e;  // the same maximum in log2 units
+  if (Mn == -INFINITY) {  // no visible key at all (prefix-only merge of an empty prefix)
     if (pg == 0)
 #pragma unroll
       for (int e = 0; e < DPL; ++e) outp[e] = 0.f;
@@ -302,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   float acc[DPL];
   float wl = 0.f;  // this group's weight sum
   {
-    const float wt = (tree_slot && pg == 0) ? __builtin_amdgcn_exp2f(lse_tree * kLog2e - M) : 0.f;
+    const float wt = (tree_slot && pg == 0) ? __builtin_amdgcn_exp2f((lse_tree - Mn) * kLog2e) : 0.f;
     wl += wt;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
@@ -313,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
     }
   }
   auto add_part = [&](float l, const float4 (&pv)[NV]) {
-    const float w = __builtin_amdgcn_exp2f(l * kLog2e - M);
+    const float w = __builtin_amdgcn_exp2f((l - Mn) * kLog2e);
     wl += w;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
@@ -357,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
       ((float4*)outp)[j] = make_float4(acc[4 * j] * inv, acc[4 * j + 1] * inv,
                                        acc[4 * j + 2] * inv, acc[4 * j + 3] * inv);
   }
-  if (lane == 0) *lsep = (M + __log2f(wsum)) * kLn2;
+  if (lane == 0) *lsep = Mn + __log2f(wsum) * kLn2;
 }
 
 template <int MODE, typename TIN>
@@ -402,7 +414,7 @@ hipError_t launch_lse_merge(const Geometry& g, const int32_t* prefix_len, bool i
                             float* out, float* lse, const Workspace& ws, hipStream_t stream) {
   MergeArgs a = {};
   a.prefix_len = prefix_len;
-  a.status = include_tree ? ws.status : nullptr;
+  a.status = ws.status;  // read always, used only with the tree partial
   a.lse_part = ws.lse_part;
   a.o_part = ws.o_part;
   a.out = out;
