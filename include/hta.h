@@ -91,10 +91,15 @@ typedef struct {
  * workspace.  Partial results of split s (s < num_splits: prefix keys
  * [s*chunk, min((s+1)*chunk, prefix_len[b])); s == num_splits: the tree keys) live at
  *   lse_part[((b*Hkv + g)*(num_splits+1) + s)*rows_padded + r]              (float)
- *   o_part  [(((b*Hkv + g)*(num_splits+1) + s)*rows_padded + r)*D + d]      (float)
+ *   o_part row (((b*Hkv + g)*(num_splits+1) + s)*rows_padded + r)          (3*D bytes)
  * where row r = i*(Hq/Hkv) + (h % (Hq/Hkv)) packs the query heads sharing KV head g.
  * o_part holds the normalised partial output, lse_part its natural-log normaliser
- * (-inf for an empty chunk).  Splits at or past ceil(prefix_len[b]/chunk) are not written. */
+ * (-inf for an empty chunk).  Splits at or past ceil(prefix_len[b]/chunk) are not written.
+ * An o_part row stores each value as the top 24 bits of its fp32 bit pattern (rounded to
+ * nearest even at bit 8; relative error at most 2^-16), values 4j..4j+3 in the three
+ * little-endian uint32 words 3j..3j+2 of the row:
+ *   w0 = x0[31:8] | x1[15:8] << 24,  w1 = x1[31:16] | x2[23:8] << 16,
+ *   w2 = x2[31:24] | x3[31:8] << 8   (x = the rounded fp32 bit patterns). */
 typedef struct {
     int32_t chunk;          /* prefix keys per split */
     int32_t num_splits;     /* ceil(max_prefix_len / chunk), at least 1 */

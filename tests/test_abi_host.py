@@ -11,6 +11,9 @@ import ctypes
 import os
 import re
 
+import numpy as np
+import torch
+
 import pytest
 
 import tree_verification_attention_amd as hta
@@ -63,7 +66,41 @@ def test_plan_llama_shape():
     # partial buffers hold (splits + 1) slots: the last one is the tree partial
     n = 8 * (p.num_splits + 1) * 272
     assert p.o_part_offset >= p.lse_part_offset + 4 * n
-    assert p.workspace_bytes >= p.o_part_offset + 4 * n * 128
+    # o_part rows: 128 values packed to 24 bits each
+    assert p.workspace_bytes >= p.o_part_offset + 3 * n * 128
+
+
+def _round24(bits: np.ndarray) -> np.ndarray:
+    """fp32 bit patterns rounded to their top 24 bits, nearest even (include/hta.h)."""
+    b = bits.astype(np.uint64)
+    r = (b + 0x7F + ((b >> 8) & 1)) & 0xFFFFFF00
+    return (r & 0xFFFFFFFF).astype(np.uint32)
+
+
+def test_partial_views_decode_the_documented_packing():
+    """The packed o_part layout written out from its description in include/hta.h (an
+    encoder of its own) and read back through partial_views, on the CPU."""
+    d = _desc(batch=1, num_q_heads=4, num_kv_heads=4, head_dim=64, tree_size=3,
+              max_prefix_len=256)
+    p = hta.plan(d)
+    n = 1 * 4 * (p.num_splits + 1) * p.rows_padded
+    rng = np.random.default_rng(5)
+    vals = (rng.standard_normal((n, 64)) * np.exp2(rng.integers(-20, 20, (n, 64)))).astype(np.float32)
+    vals[0, :4] = [0.0, -0.0, 1.0 + 2.0 ** -16, 1.0 + 3 * 2.0 ** -16]  # ties round to even
+    x = _round24(vals.view(np.uint32)).reshape(n, 16, 4)
+    x0, x1, x2, x3 = (x[..., i] for i in range(4))
+    w0 = (x0 >> 8) | ((x1 >> 8) & 0xFF) << 24
+    w1 = (x1 >> 16) | ((x2 >> 8) & 0xFFFF) << 16
+    w2 = (x2 >> 24) | (x3 >> 8) << 8
+    words = np.stack((w0, w1, w2), axis=-1).astype(np.uint32)
+    ws = torch.zeros(p.workspace_bytes, dtype=torch.uint8)
+    ws[p.o_part_offset:p.o_part_offset + 3 * n * 64] = torch.from_numpy(words.view(np.uint8).reshape(-1))
+    _, o = hta.partial_views(d, ws)
+    got = o.reshape(n, 64).numpy()
+    want = x.reshape(n, 64).view(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert got[0, 2] == 1.0 and got[0, 3] == 1.0 + 2.0 ** -14  # nearest even
+    assert np.max(np.abs(got - vals) / np.maximum(np.abs(vals), 1e-30)) <= 2.0 ** -16
 
 
 @pytest.mark.parametrize("kw,code", [

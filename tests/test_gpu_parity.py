@@ -330,7 +330,10 @@ def test_prefix_len_out_of_range_is_flagged():
 
 # ----------------------------------------------------------------------------- fp32 inputs
 
-F32_TOL = 2e-5  # exact fp32 arithmetic against the fp64 oracle
+F32_TOL = 2e-5  # exact fp32 arithmetic against the fp64 oracle (log-sum-exp)
+# outputs: the split-K partials pass through memory as 24-bit floats (relative error at most
+# 2^-16, include/hta.h), so |out - oracle| <= 2^-16 max|v| + fp32 rounding; max|v| < 6 here
+F32_OUT_TOL = 1e-4
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -342,7 +345,7 @@ def test_fp32_verify(D, G):
                seed=41 + G + D, dtype=torch.float32)
     _log(f"fp32 verify D={D} G={G}")
     out, lse = run_gpu(w, chunk=256)
-    check_rows(w, out, lse, out_tol=F32_TOL, lse_tol=F32_TOL)
+    check_rows(w, out, lse, out_tol=F32_OUT_TOL, lse_tol=F32_TOL)
 
 
 def test_fp32_entry_points_match_oracle_parts():
@@ -364,7 +367,7 @@ def test_fp32_entry_points_match_oracle_parts():
     hta.hta_merge(desc, t["prefix_len"], True, out, lse, ws)
     torch.cuda.synchronize()
     assert hta.hta_get_device_status(desc, ws) == (0, -1)
-    check_rows(w, out.cpu().double().numpy(), lse.cpu().double().numpy(), out_tol=F32_TOL,
+    check_rows(w, out.cpu().double().numpy(), lse.cpu().double().numpy(), out_tol=F32_OUT_TOL,
                lse_tol=F32_TOL)
     lse_p, o_p = (x.cpu().double().numpy() for x in hta.partial_views(desc, ws))
     info = hta.plan(desc)
@@ -375,7 +378,7 @@ def test_fp32_entry_points_match_oracle_parts():
     ro, rl = oracle.rows(w.as_numpy(), w.scale, b_idx, h_idx, i_idx, oracle.PART_TREE)
     go = o_p[0, h_idx // G, info.num_splits, i_idx * G + h_idx % G]
     gl = lse_p[0, h_idx // G, info.num_splits, i_idx * G + h_idx % G]
-    assert float(np.max(np.abs(go - ro))) <= F32_TOL
+    assert float(np.max(np.abs(go - ro))) <= F32_OUT_TOL
     assert float(np.max(np.abs(gl - rl))) <= F32_TOL
 
 

@@ -85,7 +85,7 @@ hta_status make_plan(const hta_desc* d, Geometry* g, hta_plan_info* info) {
   p.lse_part_offset = off;
   off = round_up(off + sizeof(float) * parts, 256);
   p.o_part_offset = off;
-  off = round_up(off + sizeof(float) * parts * G.D, 256);
+  off = round_up(off + 3 * parts * G.D, 256);  // packed 24-bit values
   p.workspace_bytes = off;
   if (g) *g = G;
   if (info) *info = p;
@@ -98,7 +98,7 @@ Workspace carve(void* base, const hta_plan_info& p) {
   w.status = (int32_t*)(c + p.status_offset);
   w.masks = (uint64_t*)(c + p.masks_offset);
   w.lse_part = (float*)(c + p.lse_part_offset);
-  w.o_part = (float*)(c + p.o_part_offset);
+  w.o_part = (uint32_t*)(c + p.o_part_offset);
   return w;
 }
 

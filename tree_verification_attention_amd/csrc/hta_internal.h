@@ -42,8 +42,53 @@ struct Workspace {
   int32_t* status;      // [B]
   uint64_t* masks;      // [B, T, W]
   float* lse_part;      // [B, Hkv, S+1, R_pad]
-  float* o_part;        // [B, Hkv, S+1, R_pad, D]
+  uint32_t* o_part;     // [B, Hkv, S+1, R_pad, D] packed 24-bit values: 3 D / 4 dwords a row
 };
+
+// Split-K partial outputs travel through memory as packed 24-bit floats: the top 24 bits of
+// the fp32 value (sign, 8-bit exponent, 15 mantissa bits), rounded to nearest even, four
+// values in three dwords.  The relative error is at most 2^-16 (normalised partials are
+// bounded by max |v|), and the partial traffic -- written by the prefix pass, read by the
+// merge -- is three quarters of fp32.
+struct Packed24 {
+  uint32_t w[3];
+};
+__device__ __forceinline__ uint32_t round24(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7Fu + ((u >> 8) & 1u)) & 0xFFFFFF00u;
+}
+__device__ __forceinline__ Packed24 pack24(f32x4 v) {
+  const uint32_t r0 = round24(v[0]), r1 = round24(v[1]), r2 = round24(v[2]), r3 = round24(v[3]);
+  Packed24 p;
+  p.w[0] = (r0 >> 8) | (r1 << 16);
+  p.w[1] = (r1 >> 16) | (r2 << 8);
+  p.w[2] = (r2 >> 24) | r3;
+  return p;
+}
+__device__ __forceinline__ f32x4 unpack24(Packed24 p) {
+  f32x4 v;
+  v[0] = __uint_as_float(p.w[0] << 8);
+  v[1] = __uint_as_float(((p.w[0] >> 16) | (p.w[1] << 16)) & 0xFFFFFF00u);
+  v[2] = __uint_as_float(((p.w[1] >> 8) | (p.w[2] << 24)) & 0xFFFFFF00u);
+  v[3] = __uint_as_float(p.w[2] & 0xFFFFFF00u);
+  return v;
+}
+// Store / load group g (values 4 g .. 4 g + 3) of a packed row.
+__device__ __forceinline__ void store24(uint32_t* row, int g, f32x4 v) {
+  const Packed24 p = pack24(v);
+  uint32_t* d = row + 3 * g;
+  d[0] = p.w[0];
+  d[1] = p.w[1];
+  d[2] = p.w[2];
+}
+__device__ __forceinline__ f32x4 load24(const uint32_t* row, int g) {
+  const uint32_t* s = row + 3 * g;
+  Packed24 p;
+  p.w[0] = s[0];
+  p.w[1] = s[1];
+  p.w[2] = s[2];
+  return unpack24(p);
+}
 
 // Host launchers (each enqueues exactly one kernel on the stream).
 hipError_t launch_prefix_attn_splitk(const Geometry& g, const void* q, const void* k_prefix,

@@ -43,7 +43,7 @@ struct MergeArgs {
   const int32_t* prefix_len;
   const int32_t* status;   // [B]: read by the plain merge (the tree pass status)
   float* lse_part;               // read by the merges, written by the tree-only form
-  float* o_part;
+  uint32_t* o_part;              // packed 24-bit rows (load24 / store24)
   float* out;
   float* lse;
   // fused merge only
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   constexpr bool FUSED = MODE != kPlain;   // computes the tree part
   constexpr bool PREFIX = MODE != kTreeOnly;
   constexpr int DPL = D / 16;   // output dimensions per lane of a part group
-  constexpr int NV = DPL / 4;   // float4 loads per part and lane
+  constexpr int NV = DPL / 4;   // packed 4-value groups per part and lane
   constexpr int kBatch = 9;     // splits per lane per pass: 36 per pass
   __shared__ int32_t s_par[kThreads / 64][kMaxT];  // fused: parent pointers, one slice per wave
   const Geometry& G = a.g;
@@ -120,8 +120,16 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   float* lsep = a.lse + ((size_t)b * G.Hq + h) * T + i;
   const size_t base = ((size_t)b * G.Hkv + kv) * (G.S + 1);
   const float* lrow = a.lse_part + base * G.R_pad + r;                 // slot s at s * R_pad
-  const float* orow = a.o_part + (base * G.R_pad + r) * D + DPL * dl;  // slot s at s * R_pad * D
-  const size_t ostride = (size_t)G.R_pad * D;
+  // packed partial row of slot 0 (slot s at s * ostride); this lane's groups NV dl + j
+  const uint32_t* orow = a.o_part + (base * G.R_pad + r) * (3 * D / 4);
+  const size_t ostride = (size_t)G.R_pad * (3 * D / 4);
+  auto load_groups = [&](int slot_s, Packed24 (&dst)[NV]) {
+    const uint32_t* src = orow + (size_t)slot_s * ostride + 3 * NV * dl;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int w = 0; w < 3; ++w) dst[j].w[w] = src[3 * j + w];
+  };
   const bool tree_slot = MODE == kPlain && a.include_tree;  // the plain merge's tree partial
 
   // ---- issue the loads
@@ -132,12 +140,14 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   // branch, which would serialise the loads instead of having them all in flight.
   const float lse_raw = PREFIX ? lrow[(size_t)min(lane, G.S - 1) * G.R_pad] : 0.f;
   const float lse_lane = (PREFIX && lane < G.S) ? lse_raw : -INFINITY;
-  float4 vt[NV];  // the plain merge's tree partial (slot S, always allocated)
+  Packed24 vt[NV];  // the plain merge's tree partial (slot S, always allocated)
   const float lse_tree_raw = FUSED ? 0.f : lrow[(size_t)G.S * G.R_pad];
+  if constexpr (FUSED) {
 #pragma unroll
-  for (int j = 0; j < NV; ++j)
-    vt[j] = FUSED ? make_float4(0.f, 0.f, 0.f, 0.f)
-                  : ((const float4*)(orow + (size_t)G.S * ostride))[j];
+    for (int j = 0; j < NV; ++j) vt[j] = Packed24{{0u, 0u, 0u}};
+  } else {
+    load_groups(G.S, vt);
+  }
   const float lse_tree = tree_slot ? lse_tree_raw : -INFINITY;
   int par[kMaxT / 64];
   float qv[DPL];
@@ -153,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
     for (int e = 0; e < DPL; ++e) qv[e] = to_f32(qp[e]);
   }
   float lk[kBatch];
-  float4 v[kBatch][NV];
+  Packed24 v[kBatch][NV];
   auto load_parts = [&](int k0, int k1) {
 #pragma unroll
     for (int k = k0; k < k1; ++k) {
@@ -161,11 +171,10 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
       const int p = min(pg + 4 * k, G.S - 1);
       lk[k] = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < NV; ++j) v[k][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int j = 0; j < NV; ++j) v[k][j] = Packed24{{0u, 0u, 0u}};
       if (PREFIX && 4 * k < G.S) {  // wave-uniform
         lk[k] = lrow[(size_t)p * G.R_pad];
-#pragma unroll
-        for (int j = 0; j < NV; ++j) v[k][j] = ((const float4*)(orow + (size_t)p * ostride))[j];
+        load_groups(p, v[k]);
       }
     }
   };
@@ -273,11 +282,13 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
     // (the tree partial of a rejected tree is NaN)
     const float ltot = group_sum4(lt);
     const float inv = 1.f / ltot;
-    float* tp = a.o_part + ((base + G.S) * G.R_pad + r) * D + DPL * dl;
+    uint32_t* trow = a.o_part + ((base + G.S) * G.R_pad + r) * (3 * D / 4);
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      const float o = group_sum4(at[e]) * inv;
-      if (pg == 0) tp[e] = bad ? NAN : o;
+    for (int j = 0; j < NV; ++j) {
+      f32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = bad ? NAN : group_sum4(at[4 * j + e]) * inv;
+      if (pg == 0) store24(trow, NV * dl + j, o);
     }
     if (lane == 0)
       a.lse_part[(base + G.S) * G.R_pad + r] = bad ? NAN : (mt + __log2f(ltot)) * kLn2;
@@ -318,21 +329,19 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
     wl += wt;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      acc[4 * j + 0] = wt * vt[j].x;
-      acc[4 * j + 1] = wt * vt[j].y;
-      acc[4 * j + 2] = wt * vt[j].z;
-      acc[4 * j + 3] = wt * vt[j].w;
+      const f32x4 t = unpack24(vt[j]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 * j + e] = wt * t[e];
     }
   }
-  auto add_part = [&](float l, const float4 (&pv)[NV]) {
+  auto add_part = [&](float l, const Packed24 (&pv)[NV]) {
     const float w = __builtin_amdgcn_exp2f((l - Mn) * kLog2e);
     wl += w;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      acc[4 * j + 0] += w * pv[j].x;
-      acc[4 * j + 1] += w * pv[j].y;
-      acc[4 * j + 2] += w * pv[j].z;
-      acc[4 * j + 3] += w * pv[j].w;
+      const f32x4 t = unpack24(pv[j]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 * j + e] += w * t[e];
     }
   };
 #pragma unroll
@@ -345,8 +354,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
       const int p = p0 + 4 * k;
       if (p < nsplit) {
         lk[k] = lrow[(size_t)p * G.R_pad];
-#pragma unroll
-        for (int j = 0; j < NV; ++j) v[k][j] = ((const float4*)(orow + (size_t)p * ostride))[j];
+        load_groups(p, v[k]);
       }
     }
 #pragma unroll

@@ -26,7 +26,7 @@ struct PrefixF32Args {
   const float* v_prefix;
   const int32_t* prefix_len;
   float* lse_part;
-  float* o_part;
+  uint32_t* o_part;  // packed 24-bit rows (store24)
   Geometry g;
 };
 
@@ -97,9 +97,14 @@ __global__ __launch_bounds__(64 * kWaves) void prefix_attn_f32(PrefixF32Args a) 
       }
     }
     const float inv = 1.f / l;
-    float* op = a.o_part + (slot * G.R_pad + r) * D + lane;
+    // lane owns dims lane + 64 e; every fourth lane packs its group of four
+    uint32_t* orow = a.o_part + (slot * G.R_pad + r) * (3 * D / 4);
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) op[64 * e] = acc[e] * inv;
+    for (int e = 0; e < DPL; ++e) {
+      const float x = acc[e] * inv;
+      const f32x4 g4 = {x, __shfl_down(x, 1), __shfl_down(x, 2), __shfl_down(x, 3)};
+      if ((lane & 3) == 0) store24(orow, (lane + 64 * e) / 4, g4);
+    }
     if (lane == 0) a.lse_part[slot * G.R_pad + r] = (m + __log2f(l)) * kLn2;
     __builtin_amdgcn_wave_barrier();  // s_q is rewritten for the next row
   }

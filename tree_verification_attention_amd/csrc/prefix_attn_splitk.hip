@@ -117,7 +117,7 @@ struct PrefixArgs {
   const unsigned short* v_prefix;
   const int32_t* prefix_len;       // [B]
   float* lse_part;
-  float* o_part;
+  uint32_t* o_part;                // packed 24-bit rows (store24)
   Geometry g;
   int32_t row_blocks;              // query-row blocks per (b, kv head)
   int32_t tiles_per_block;         // row tiles per block
@@ -581,13 +581,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   // ---- normalise and write this chunk's partial
   const size_t slot = ((size_t)b * G.Hkv + kv) * (G.S + 1) + s;
   // A lane holds 4 consecutive dims of one row per d block, so direct stores would write
-  // 64-byte pieces of 16 rows per instruction.  Each wave stages its normalised rows in LDS
+  // small pieces of 16 rows per instruction.  Each wave stages its normalised rows in LDS
   // (the V and V^T rings are free once every wave is past its loop) and writes them back
-  // whole: every store instruction covers 1 KB of consecutive rows.
+  // whole, packed to 24 bits: every store instruction covers consecutive rows (two at
+  // D = 128, 768 bytes).
   __syncthreads();
   {
     constexpr int kC = D / 4;                        // 16-byte chunks per fp32 row
-    constexpr int kRowsPerInst = 64 * 16 / (D * 4);  // rows per 1 KB store instruction
+    constexpr int kRowsPerInst = 64 * 16 / (D * 4);  // rows per store instruction
     static_assert(Y::kVRing + kWaves * 16 * D * 4 <= Y::kBytes, "staging fits the V rings");
     unsigned char* stage = lds + Y::kVRing + wave * (16 * D * 4);
 #pragma unroll
@@ -606,7 +607,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
       for (int j = 0; j < 16 / kRowsPerInst; ++j) {
         const int rr = j * kRowsPerInst + lane / kC, c = lane % kC;
         const f32x4 v = *(const f32x4*)(stage + rr * D * 4 + 16 * (c ^ (rr & (kC - 1))));
-        *(f32x4*)(a.o_part + (slot * G.R_pad + tile * 16 + rr) * D + 4 * c) = v;
+        store24(a.o_part + (slot * G.R_pad + tile * 16 + rr) * (3 * D / 4), c, v);
       }
       if (grp == 0) a.lse_part[slot * G.R_pad + tile * 16 + l16] = (m_ref[k] + __log2f(lt)) * kLn2;
     }
@@ -649,14 +650,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
       }
       const float inv = 1.f / den;
       const int row = ltile * 16 + l16;
-      float* op = a.o_part + (slot * G.R_pad + row) * D + 4 * grp;
+      uint32_t* orow = a.o_part + (slot * G.R_pad + row) * (3 * D / 4);
 #pragma unroll
       for (int j = 0; j < kOwn; ++j) {
         f32x4 o = zero4;
 #pragma unroll
         for (int i = 0; i < kShare; ++i)
           o += wgt[i] * *(const f32x4*)(xl + ((w0 + i) * 64 + lane) * kStride + 4 * (o0 + j));
-        *(f32x4*)(op + 16 * (o0 + j)) = o * inv;
+        store24(orow, 4 * (o0 + j) + grp, o * inv);
       }
       if (grp == 0 && o0 == 0) a.lse_part[slot * G.R_pad + row] = (M + __log2f(den)) * kLn2;
     }

@@ -46,7 +46,7 @@ struct TreeArgs {
   int32_t* status;                // [B]
   uint64_t* masks_out;            // [B, T, W] or null
   float* lse_part;
-  float* o_part;
+  uint32_t* o_part;               // packed 24-bit rows (store24)
   Geometry g;
   int32_t attention;              // 0: masks and status only
 };
@@ -169,12 +169,12 @@ __global__ __launch_bounds__(kThreads) void tree_attn_masked(TreeArgs a) {
 
   if (rt >= G.NT) return;
   const size_t slot = ((size_t)b * G.Hkv + kv) * (G.S + 1) + G.S;
-  float* op = a.o_part + (slot * G.R_pad + row) * D + 4 * grp;
+  uint32_t* orow = a.o_part + (slot * G.R_pad + row) * (3 * D / 4);
   if (tree_bad) {
     if (row_ok) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        *(f32x4*)(op + 16 * db) = f32x4{NAN, NAN, NAN, NAN};
+        store24(orow, 4 * db + grp, f32x4{NAN, NAN, NAN, NAN});
       if (grp == 0) a.lse_part[slot * G.R_pad + row] = NAN;
     }
     return;
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_masked(TreeArgs a) {
   if (!row_ok) return;
   const float inv = 1.f / lt;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) *(f32x4*)(op + 16 * db) = acc[db] * inv;
+  for (int db = 0; db < DB; ++db) store24(orow, 4 * db + grp, acc[db] * inv);
   if (grp == 0) a.lse_part[slot * G.R_pad + row] = (m_run + __log2f(lt)) * kLn2;
 }
 
