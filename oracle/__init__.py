@@ -4,8 +4,10 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench
 import this package.  The HIP library and its Python binding never do: the two sides
 share nothing but the seeded input generators.
 
-The arithmetic lives in ``hta_oracle.c`` (plain C, fp64, single-threaded; its header
-states the definition and the passages it follows).  This module only builds it with gcc,
+The arithmetic lives in ``hta_oracle.c`` (the attention) and ``step_oracle.c`` (the steps
+around it: rotary positions of the tree, the target's argmax, greedy acceptance); both are
+plain C, fp64, single-threaded, and their headers state the definitions and the passages
+they follow.  ``kv_commit`` below is plain numpy indexing.  This module only builds it with gcc,
 loads it with ctypes and marshals numpy arrays.  ``bruteforce.py`` is an independent
 pure-Python version used to pin the C code on tiny inputs.
 """
@@ -20,6 +22,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "hta_oracle.c")
+_SRC_STEP = os.path.join(_HERE, "step_oracle.c")
 _LIB = os.path.join(_HERE, "libhta_oracle.so")
 
 PART_ALL, PART_PREFIX, PART_TREE = 0, 1, 2
@@ -36,7 +39,7 @@ def build(force: bool = True) -> str:
         tmp = _LIB + ".tmp"
         subprocess.check_call(
             ["gcc", "-O2", "-fno-fast-math", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
-             _SRC, "-o", tmp, "-lm"]
+             _SRC, _SRC_STEP, "-o", tmp, "-lm"]
         )
         os.replace(tmp, _LIB)
     return _LIB
@@ -57,8 +60,16 @@ def configure(L: ctypes.CDLL) -> ctypes.CDLL:
     L.hta_oracle_check_tree.argtypes = [i, i, P]
     L.hta_oracle_masked_attention.argtypes = [i, i, i, P, P, P, P, ctypes.c_double, P, P]
     L.hta_oracle_lse_merge.argtypes = [i, i, P, P, P, P]
+    L.step_oracle_depths.argtypes = [i, i, P, P]
+    L.step_oracle_rope.argtypes = [i, i, i, i, i, i, P, P, P, ctypes.c_double, i, P, P]
+    L.step_oracle_round_bf16.argtypes = [ctypes.c_size_t, P, P]
+    L.step_oracle_round_bf16.restype = None
+    L.step_oracle_argmax.argtypes = [i, i, i, P, P]
+    L.step_oracle_accept.argtypes = [i, i, P, P, P, P, P, P, P]
     for f in (L.hta_oracle_rows, L.hta_oracle_verify, L.hta_oracle_masks,
-              L.hta_oracle_check_tree, L.hta_oracle_masked_attention, L.hta_oracle_lse_merge):
+              L.hta_oracle_check_tree, L.hta_oracle_masked_attention, L.hta_oracle_lse_merge,
+              L.step_oracle_depths, L.step_oracle_rope, L.step_oracle_argmax,
+              L.step_oracle_accept):
         f.restype = ctypes.c_int
     return L
 
@@ -66,7 +77,8 @@ def configure(L: ctypes.CDLL) -> ctypes.CDLL:
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(
+                os.path.getmtime(_SRC), os.path.getmtime(_SRC_STEP)):
             build(force=True)
         _lib = configure(ctypes.CDLL(_LIB))
     return _lib
@@ -187,3 +199,116 @@ def lse_merge(lse_parts: np.ndarray, o_parts: np.ndarray) -> Tuple[np.ndarray, f
     lse = np.empty((1,), dtype=np.float64)
     _check(lib().hta_oracle_lse_merge(n, D, _ptr(l), _ptr(o), _ptr(out), _ptr(lse)))
     return out, float(lse[0])
+
+
+# ----------------------------------------------------------------------------- around the attention
+
+
+def depths(parent_idx: np.ndarray) -> np.ndarray:
+    """Depth of every tree node (0 for a node whose parent is -1), int32 [B, T]."""
+    par = np.ascontiguousarray(parent_idx, dtype=np.int32)
+    B, T = par.shape
+    d = np.empty((B, T), dtype=np.int32)
+    _check(lib().step_oracle_depths(B, T, _ptr(par), _ptr(d)))
+    return d
+
+
+def rope(x: np.ndarray, parent_idx: np.ndarray, prefix_len: np.ndarray, theta: float,
+         interleaved: bool = False, layout: str = "q") -> Tuple[np.ndarray, np.ndarray]:
+    """Rotary encoding of tree rows at positions prefix_len + depth, exact in fp64.
+
+    x: bf16 bits (uint16) or float32, [B, T, H, D] for layout "q", [B, H, T, D] for "k".
+    Returns (rotated fp64 array of x's shape, positions int32 [B, T])."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        is_bf16 = 1
+    elif x.dtype == np.float32:
+        is_bf16 = 0
+    else:
+        raise TypeError("x must be bf16 bits (uint16) or float32")
+    par = np.ascontiguousarray(parent_idx, dtype=np.int32)
+    pl = np.ascontiguousarray(prefix_len, dtype=np.int32)
+    if layout == "q":
+        B, T, H, D = x.shape
+        lay = 0
+    elif layout == "k":
+        B, H, T, D = x.shape
+        lay = 1
+    else:
+        raise ValueError(layout)
+    assert par.shape == (B, T) and pl.shape == (B,)
+    out = np.empty(x.shape, dtype=np.float64)
+    pos = np.empty((B, T), dtype=np.int32)
+    rc = lib().step_oracle_rope(B, T, H, D, lay, is_bf16, _ptr(x), _ptr(par), _ptr(pl),
+                                float(theta), 1 if interleaved else 0, _ptr(out), _ptr(pos))
+    _check(rc)
+    return out, pos
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """fp64 -> bf16 bit patterns (uint16), nearest-even, one rounding."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().step_oracle_round_bf16(x.size, _ptr(x), _ptr(out))
+    return out
+
+
+def argmax(logits: np.ndarray) -> np.ndarray:
+    """Greedy token of each row of logits [..., V] (bf16 bits or float32): first maximum,
+    NaN largest.  Returns int32 of shape logits.shape[:-1]."""
+    lg = np.ascontiguousarray(logits)
+    if lg.dtype == np.uint16:
+        is_bf16 = 1
+    elif lg.dtype == np.float32:
+        is_bf16 = 0
+    else:
+        raise TypeError("logits must be bf16 bits (uint16) or float32")
+    V = lg.shape[-1]
+    rows = lg.size // V
+    idx = np.empty(lg.shape[:-1], dtype=np.int32)
+    _check(lib().step_oracle_argmax(rows, V, is_bf16, _ptr(lg), _ptr(idx)))
+    return idx
+
+
+def accept(parent_idx: np.ndarray, tokens: np.ndarray, root_token: np.ndarray,
+           target_next: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Greedy acceptance along each tree: (accept_len [B], accepted [B, T] (-1 padded),
+    bonus [B]), all int32."""
+    par = np.ascontiguousarray(parent_idx, dtype=np.int32)
+    tok = np.ascontiguousarray(tokens, dtype=np.int32)
+    root = np.ascontiguousarray(root_token, dtype=np.int32)
+    nxt = np.ascontiguousarray(target_next, dtype=np.int32)
+    B, T = par.shape
+    assert tok.shape == (B, T) and nxt.shape == (B, T) and root.shape == (B,)
+    n = np.empty((B,), dtype=np.int32)
+    acc = np.empty((B, T), dtype=np.int32)
+    bonus = np.empty((B,), dtype=np.int32)
+    _check(lib().step_oracle_accept(B, T, _ptr(par), _ptr(tok), _ptr(root), _ptr(nxt), _ptr(n),
+                                    _ptr(acc), _ptr(bonus)))
+    return n, acc, bonus
+
+
+def kv_commit(k_prefix: np.ndarray, v_prefix: np.ndarray, k_tree: np.ndarray,
+              v_tree: np.ndarray, prefix_len: np.ndarray, accept_len: np.ndarray,
+              accepted: np.ndarray):
+    """Append the accepted path's tree keys and values to each sequence's prefix cache.
+
+    Row k of the path (node accepted[b, k]) goes to cache row prefix_len[b] + k of every KV
+    head, and prefix_len[b] grows by accept_len[b].  A sequence whose cache cannot hold the
+    path (prefix_len + accept_len > Lmax) is left unchanged and reported in the returned
+    ``full`` flags.  Returns new arrays (k_prefix, v_prefix, prefix_len, full)."""
+    kp, vp = k_prefix.copy(), v_prefix.copy()
+    pl = np.array(prefix_len, dtype=np.int32, copy=True)
+    B, Hkv, Lmax, D = kp.shape
+    full = np.zeros((B,), dtype=bool)
+    for b in range(B):
+        L, n = int(prefix_len[b]), int(accept_len[b])
+        if L + n > Lmax:
+            full[b] = True
+            continue
+        for k in range(n):
+            node = int(accepted[b, k])
+            kp[b, :, L + k, :] = k_tree[b, :, node, :]
+            vp[b, :, L + k, :] = v_tree[b, :, node, :]
+        pl[b] = L + n
+    return kp, vp, pl, full

@@ -26,6 +26,7 @@ from tree_verification_attention_amd import workloads as W
 from helpers import f64, tiny_workload
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "hta_oracle.c")
+STEP_SRC = os.path.join(os.path.dirname(oracle.__file__), "step_oracle.c")
 
 MUTANTS = {
     "self_bit_dropped": ("for (int p = i; p != -1; p = par[p])\n                in_tree[p] = 1;",
@@ -143,7 +144,7 @@ def test_each_mutant_fails_a_pin(name, tmp_path):
     so = tmp_path / "libmutant.so"
     c.write_text(mutated)
     subprocess.check_call(["gcc", "-O2", "-fno-fast-math", "-std=c11", "-shared", "-fPIC",
-                           str(c), "-o", str(so), "-lm"])
+                           str(c), STEP_SRC, "-o", str(so), "-lm"])
     failed = []
     with swapped(str(so)):
         for pin in PINS:

@@ -219,6 +219,72 @@ def make_workload(
     )
 
 
+# ----------------------------------------------------------------------------- step inputs
+
+# Vocabulary sizes and rotary bases of the checkpoints the LongSpec README evaluates (from
+# their public model configurations): Llama-3-8B, Vicuna-7B (a Llama-2 model), QwQ-32B.
+LLAMA3_VOCAB, VICUNA_VOCAB, QWQ_VOCAB = 128256, 32000, 152064
+LLAMA3_ROPE_THETA, VICUNA_ROPE_THETA, QWQ_ROPE_THETA = 500000.0, 10000.0, 1000000.0
+
+
+@dataclasses.dataclass
+class StepInputs:
+    """What one greedy verification step needs besides the attention inputs (CPU tensors).
+
+    ``tokens`` [B, T] int32: the drafted token of every tree node; ``root_token`` [B] int32:
+    the target's token for the position after the prefix (known from the previous step);
+    ``logits`` [B, T, V]: the target's scores after every node; ``planted`` [B, T] int32:
+    the token whose score was raised above every other in that row."""
+
+    tokens: torch.Tensor
+    root_token: torch.Tensor
+    logits: torch.Tensor
+    planted: torch.Tensor
+
+    @property
+    def vocab(self) -> int:
+        return self.logits.shape[-1]
+
+
+def make_step_inputs(parents: Sequence[Sequence[int]], vocab: int, *, p_root: float = 0.95,
+                     p_follow: float = 0.85, dtype: torch.dtype = torch.bfloat16,
+                     planted_score: float = 12.0, seed: int = 0) -> StepInputs:
+    """Draw tokens and logits for a batch of draft trees.
+
+    Draw order (fixed): tokens uniform in [0, vocab); per sequence a Bernoulli(``p_root``)
+    and a uniform root choice -- on success ``root_token`` is that root's token, otherwise a
+    uniform token; per node a Bernoulli(``p_follow``) and a uniform child choice -- on
+    success (and if the node has children) the planted token is that child's token,
+    otherwise a uniform token; then N(0, 1) logits.  The planted token's score is set to
+    ``planted_score`` (above every N(0, 1) draw of a realistic vocabulary).  With the
+    defaults the greedy walk accepts about 2.4 of the 5 levels of the 4,16,16,16,16 tree
+    (3.4 tokens a step with the target's own token), near the mean acceptance length of
+    about 3.8 the LongSpec paper summary reports for QwQ-32B."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    B = len(parents)
+    T = len(parents[0])
+    tokens = torch.randint(0, vocab, (B, T), generator=gen, dtype=torch.int64)
+    root = torch.empty(B, dtype=torch.int64)
+    planted = torch.empty(B, T, dtype=torch.int64)
+    for b in range(B):
+        par = list(parents[b])
+        roots = [i for i in range(T) if par[i] == -1]
+        hit = bool(torch.rand(1, generator=gen) < p_root)
+        pick = int(torch.randint(0, max(len(roots), 1), (1,), generator=gen))
+        other = int(torch.randint(0, vocab, (1,), generator=gen))
+        root[b] = int(tokens[b, roots[pick]]) if (hit and roots) else other
+        for i in range(T):
+            kids = [c for c in range(T) if par[c] == i]
+            hit = bool(torch.rand(1, generator=gen) < p_follow)
+            pick = int(torch.randint(0, max(len(kids), 1), (1,), generator=gen))
+            other = int(torch.randint(0, vocab, (1,), generator=gen))
+            planted[b, i] = int(tokens[b, kids[pick]]) if (hit and kids) else other
+    logits = torch.randn(B, T, vocab, generator=gen)
+    logits.scatter_(2, planted.unsqueeze(-1), planted_score)
+    return StepInputs(tokens=tokens.to(torch.int32), root_token=root.to(torch.int32),
+                      logits=logits.to(dtype).contiguous(), planted=planted.to(torch.int32))
+
+
 # ----------------------------------------------------------------------------- named configs
 
 QWQ_PREFIXES = (4096, 8192, 16384, 32768)
