@@ -69,7 +69,8 @@ typedef enum {
     HTA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than hta_workspace_size() */
     HTA_ERR_TREE = 6,        /* (device) a parent pointer outside [-1, i-1] */
     HTA_ERR_PREFIX_LEN = 7,  /* (device) prefix_len[b] outside [0, max_prefix_len] */
-    HTA_ERR_HIP = 8          /* a HIP runtime call failed */
+    HTA_ERR_HIP = 8,         /* a HIP runtime call failed */
+    HTA_ERR_CACHE_FULL = 9   /* (device) prefix_len[b] + accepted nodes > max_prefix_len */
 } hta_status;
 
 typedef enum { HTA_BF16 = 0, HTA_F32 = 1 } hta_dtype;
@@ -172,10 +173,82 @@ hta_status hta_merge(const hta_desc *desc, const int32_t *prefix_len, int32_t in
                      void *stream);
 
 /*
+ * ---- The steps on either side of the attention in one greedy verification step ----
+ *
+ * Speculative decoding at temperature 0 (LongSpec README, Evaluation: both inference
+ * commands pass --temperature 0 and --tree_shape 4 16 16 16 16) verifies a draft tree as
+ * follows: the tree's queries and keys are position-encoded at the tree positions, the
+ * attention above runs, the target's greedy token after every node is read off its logits,
+ * the longest drafted path that agrees with those tokens is accepted, and the accepted
+ * path's keys and values join the prefix cache.  The emitted tokens are exactly those plain
+ * greedy decoding emits (the lossless property, README title).
+ */
+
+/*
+ * Rotary position encoding of the draft tree, in place (RoFormer, cited by the LongSpec
+ * paper).  Node i of sequence b sits at position prefix_len[b] + depth(i), depth 0 for a
+ * node whose parent is -1.  Pair j of every head vector of q [B,T,Hq,D] and k_tree
+ * [B,Hkv,T,D] (in_dtype) is turned by the angle position * rope_theta^(-2j/D):
+ *     (x_a, x_c) -> (x_a cos - x_c sin, x_c cos + x_a sin)
+ * with pairs (a, c) = (j, j + D/2) when interleaved == 0 (the Llama / Qwen layout) and
+ * (2j, 2j + 1) when interleaved != 0.  Angles and products are evaluated in fp64 and each
+ * result is rounded once to in_dtype (nearest even), so positions far beyond 2^16 keep
+ * their accuracy.  positions (device int32 [B, T], may be NULL) receives the positions.
+ * Device errors (an invalid tree, prefix_len outside [0, Lmax]) are recorded in the
+ * workspace status (read with hta_get_device_status) and make that sequence's q and k_tree
+ * rows NaN and its positions -1.  Only the status words at the start of the workspace are
+ * written: any buffer of at least 4 * batch bytes rounded up to 256 serves (a workspace of
+ * hta_verify does).  rope_theta must be positive and finite.
+ */
+hta_status hta_rope_tree(const hta_desc *desc, double rope_theta, int32_t interleaved, void *q,
+                         void *k_tree, const int32_t *parent_idx, const int32_t *prefix_len,
+                         int32_t *positions, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* Workspace bytes for hta_accept_commit with this vocabulary size (0 if invalid); at least
+ * hta_workspace_size(desc), so one buffer of this size serves every entry point. */
+size_t hta_accept_workspace_size(const hta_desc *desc, int32_t vocab);
+
+/*
+ * Greedy acceptance and KV commit (temperature 0; README, Evaluation).
+ *   logits      [B, T, vocab]  logits_dtype (HTA_BF16 or HTA_F32): the target's scores for
+ *                              the token after every tree node
+ *   tokens      [B, T]  int32  the drafted token of every node
+ *   root_token  [B]     int32  the target's greedy token for the position after the prefix
+ * Outputs (device int32):
+ *   target_next [B, T]  index of the largest logit of each row; ties go to the smallest
+ *                       index, +0 equals -0, and a NaN counts as larger than any number
+ *   accept_len  [B]     accepted nodes n: the walk starts from the prefix expecting
+ *                       root_token[b]; while some child of the last accepted node (a root,
+ *                       at the start) carries the expected token, the one with the smallest
+ *                       index is accepted and target_next of it becomes the expected token
+ *   accepted    [B, T]  the accepted nodes in path order, -1 past n
+ *   bonus_token [B]     the expected token after the last accepted node (the target's own
+ *                       token, emitted in addition to the n accepted ones)
+ * KV commit, in place: row k < n of the path (node accepted[b,k]) of k_tree / v_tree is
+ * copied to row prefix_len[b] + k of k_prefix / v_prefix for every KV head (in_dtype), and
+ * prefix_len[b] grows by n.  The bonus token has no key or value yet and is not committed.
+ * Device errors, recorded in the workspace status: an invalid tree (n = 0, accepted all -1,
+ * bonus -1, nothing committed), prefix_len outside [0, Lmax] or a path that does not fit
+ * (HTA_ERR_CACHE_FULL): the acceptance outputs are written, the cache and prefix_len are
+ * left unchanged.  Any vocab >= 1 (rows whose byte length is a multiple of 16 and a
+ * 16-byte aligned logits pointer take the vector path).  The workspace must hold
+ * hta_accept_workspace_size(desc, vocab) bytes.
+ */
+hta_status hta_accept_commit(const hta_desc *desc, int32_t vocab, int32_t logits_dtype,
+                             const void *logits, const int32_t *tokens,
+                             const int32_t *root_token, const int32_t *parent_idx,
+                             int32_t *prefix_len, void *k_prefix, void *v_prefix,
+                             const void *k_tree, const void *v_tree, int32_t *target_next,
+                             int32_t *accept_len, int32_t *accepted, int32_t *bonus_token,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Synchronise the stream, read the device status the last hta_verify / hta_tree_partials /
- * hta_ancestor_masks call left in the workspace, and return HTA_OK, HTA_ERR_TREE or
- * HTA_ERR_PREFIX_LEN (tree errors reported first).  *bad_sequence (if not NULL) receives
- * the first offending batch index, or -1.
+ * hta_ancestor_masks / hta_rope_tree / hta_accept_commit call left in the workspace, and
+ * return HTA_OK, HTA_ERR_TREE, HTA_ERR_PREFIX_LEN or HTA_ERR_CACHE_FULL (reported in that
+ * order of precedence).  *bad_sequence (if not NULL) receives the first offending batch
+ * index, or -1.
  */
 hta_status hta_get_device_status(const hta_desc *desc, const void *workspace, void *stream,
                                  int32_t *bad_sequence);

@@ -195,3 +195,55 @@ def test_other_entry_points_validate_before_launching():
 
 def test_version():
     assert hta.load().hta_version() >= 100
+
+
+def test_rope_tree_validates_before_launching():
+    L = hta.load()
+    d = _desc()
+    small = 256  # the status words of one sequence
+    args = lambda **kw: [kw.get("theta", 500000.0), 0, kw.get("q", FAKE), kw.get("k", FAKE),  # noqa: E731
+                         kw.get("par", FAKE), kw.get("pl", FAKE), kw.get("pos", None),
+                         kw.get("ws", FAKE), kw.get("n", small), None]
+    assert L.hta_rope_tree(ctypes.byref(d), *args(q=None)) == NULL
+    assert L.hta_rope_tree(ctypes.byref(d), *args(k=FAKE + 2)) == ALIGN
+    assert L.hta_rope_tree(ctypes.byref(d), *args(pos=FAKE + 4)) == ALIGN
+    assert L.hta_rope_tree(ctypes.byref(d), *args(theta=0.0)) == SHAPE
+    assert L.hta_rope_tree(ctypes.byref(d), *args(theta=float("inf"))) == SHAPE
+    assert L.hta_rope_tree(ctypes.byref(d), *args(theta=float("nan"))) == SHAPE
+    assert L.hta_rope_tree(ctypes.byref(d), *args(n=small - 1)) == WORKSPACE
+    assert L.hta_rope_tree(ctypes.byref(d), *args(ws=FAKE + 16)) == ALIGN
+    assert L.hta_rope_tree(ctypes.byref(_desc(head_dim=80)), *args()) == SHAPE
+
+
+def test_accept_workspace_size():
+    d = _desc()
+    base = hta.workspace_size(d)
+    # fp32 logits: 4096-element spans; Llama-3's 128256 -> 32 spans per row, 68 rows
+    n = hta.accept_workspace_size(d, 128256)
+    assert n >= base + 8 * 68 * 32 and n % 256 == 0
+    assert hta.accept_workspace_size(d, 1) >= base + 8 * 68
+    assert hta.accept_workspace_size(d, 0) == 0
+    assert hta.accept_workspace_size(_desc(tree_size=0), 100) == 0
+
+
+def test_accept_commit_validates_before_launching():
+    L = hta.load()
+    d = _desc()
+    n = hta.accept_workspace_size(d, 128256)
+
+    def code(vocab=128256, dtype=0, i=None, val=None, ws=FAKE, nbytes=n, desc=d):
+        p = [FAKE] * 13
+        if i is not None:
+            p[i] = val
+        return L.hta_accept_commit(ctypes.byref(desc), vocab, dtype, *p, ws, nbytes, None)
+
+    for i in range(13):
+        assert code(i=i, val=None) == NULL, i
+    for i in range(1, 13):  # logits only need element alignment
+        assert code(i=i, val=FAKE + 4) == ALIGN, i
+    assert code(vocab=0) == SHAPE
+    assert code(dtype=5) == DTYPE
+    assert code(dtype=1, nbytes=n - 1) == WORKSPACE  # fp32 logits need the most spans
+    assert code(ws=None) == WORKSPACE
+    assert code(ws=FAKE + 64) == ALIGN
+    assert code(desc=_desc(num_q_heads=30)) == SHAPE

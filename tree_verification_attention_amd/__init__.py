@@ -2,17 +2,22 @@
 
 The compute path is ``libhta.so``: hand-written gfx950 HIP kernels behind the C ABI of
 ``include/hta.h``.  ``binding`` is its thin ctypes binding (same entry-point names);
-``workloads`` draws the seeded synthetic inputs.  The shared library is loaded on first
+``workloads`` draws the seeded synthetic inputs.  Around the attention, ``rope_tree`` encodes
+the tree's positions and ``accept_commit`` accepts the greedy path and grows the KV cache.  The shared library is loaded on first
 use and its absence is an error -- there is no CPU fallback.
 """
 from .binding import (  # noqa: F401
     HtaError,
+    accept_commit,
+    accept_workspace_size,
     ancestor_masks,
     desc_for,
+    hta_accept_commit,
     hta_ancestor_masks,
     hta_get_device_status,
     hta_merge,
     hta_prefix_partials,
+    hta_rope_tree,
     hta_tree_partials,
     hta_verify,
     load,
@@ -20,13 +25,16 @@ from .binding import (  # noqa: F401
     new_workspace,
     partial_views,
     plan,
+    rope_tree,
     status_str,
     verify,
     workspace_size,
 )
 
 __all__ = [
-    "HtaError", "ancestor_masks", "desc_for", "hta_ancestor_masks", "hta_get_device_status",
-    "hta_merge", "hta_prefix_partials", "hta_tree_partials", "hta_verify", "load", "make_desc",
-    "new_workspace", "partial_views", "plan", "status_str", "verify", "workspace_size",
+    "HtaError", "accept_commit", "accept_workspace_size", "ancestor_masks", "desc_for",
+    "hta_accept_commit", "hta_ancestor_masks", "hta_get_device_status", "hta_merge",
+    "hta_prefix_partials", "hta_rope_tree", "hta_tree_partials", "hta_verify", "load",
+    "make_desc", "new_workspace", "partial_views", "plan", "rope_tree", "status_str", "verify",
+    "workspace_size",
 ]

@@ -27,6 +27,7 @@ STATUS_NAMES = {
     6: "HTA_ERR_TREE",
     7: "HTA_ERR_PREFIX_LEN",
     8: "HTA_ERR_HIP",
+    9: "HTA_ERR_CACHE_FULL",
 }
 EXPORTED = (
     "hta_plan",
@@ -37,6 +38,9 @@ EXPORTED = (
     "hta_tree_partials",
     "hta_merge",
     "hta_get_device_status",
+    "hta_rope_tree",
+    "hta_accept_workspace_size",
+    "hta_accept_commit",
     "hta_status_str",
     "hta_version",
 )
@@ -101,11 +105,16 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.hta_tree_partials.argtypes = [D, P, P, P, P, P, P, S, P]
     L.hta_merge.argtypes = [D, P, I, P, P, P, S, P]
     L.hta_get_device_status.argtypes = [D, P, P, ctypes.POINTER(ctypes.c_int32)]
+    L.hta_rope_tree.argtypes = [D, ctypes.c_double, I, P, P, P, P, P, P, S, P]
+    L.hta_accept_workspace_size.argtypes = [D, I]
+    L.hta_accept_workspace_size.restype = S
+    L.hta_accept_commit.argtypes = [D, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
     L.hta_status_str.argtypes = [ctypes.c_int]
     L.hta_status_str.restype = ctypes.c_char_p
     L.hta_version.argtypes = []
     for f in (L.hta_plan, L.hta_verify, L.hta_ancestor_masks, L.hta_prefix_partials,
-              L.hta_tree_partials, L.hta_merge, L.hta_get_device_status, L.hta_version):
+              L.hta_tree_partials, L.hta_merge, L.hta_get_device_status, L.hta_version,
+              L.hta_rope_tree, L.hta_accept_commit):
         f.restype = ctypes.c_int
     _lib = L
     return L
@@ -225,6 +234,36 @@ def hta_get_device_status(desc, workspace, stream=None) -> Tuple[int, int]:
     return int(code), int(bad.value)
 
 
+def hta_rope_tree(desc, rope_theta: float, interleaved: bool, q, k_tree, parent_idx, prefix_len,
+                  positions, workspace, stream=None) -> None:
+    _contig(q, k_tree, parent_idx, prefix_len, workspace)
+    if positions is not None:
+        _contig(positions)
+    _check(load().hta_rope_tree(ctypes.byref(desc), float(rope_theta), 1 if interleaved else 0,
+                                _ptr(q), _ptr(k_tree), _ptr(parent_idx), _ptr(prefix_len),
+                                _ptr(positions), _ptr(workspace), workspace.numel(),
+                                _stream(stream)), "hta_rope_tree")
+
+
+def accept_workspace_size(desc: hta_desc, vocab: int) -> int:
+    return int(load().hta_accept_workspace_size(ctypes.byref(desc), int(vocab)))
+
+
+def hta_accept_commit(desc, logits, tokens, root_token, parent_idx, prefix_len, k_prefix,
+                      v_prefix, k_tree, v_tree, target_next, accept_len, accepted, bonus_token,
+                      workspace, stream=None) -> None:
+    _contig(logits, tokens, root_token, parent_idx, prefix_len, k_prefix, v_prefix, k_tree,
+            v_tree, target_next, accept_len, accepted, bonus_token, workspace)
+    vocab = logits.shape[-1]
+    _check(load().hta_accept_commit(ctypes.byref(desc), int(vocab), _dtype_code(logits),
+                                    _ptr(logits), _ptr(tokens), _ptr(root_token),
+                                    _ptr(parent_idx), _ptr(prefix_len), _ptr(k_prefix),
+                                    _ptr(v_prefix), _ptr(k_tree), _ptr(v_tree),
+                                    _ptr(target_next), _ptr(accept_len), _ptr(accepted),
+                                    _ptr(bonus_token), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)), "hta_accept_commit")
+
+
 # ----------------------------------------------------------------------------- convenience
 
 
@@ -255,6 +294,50 @@ def ancestor_masks(parent_idx: torch.Tensor, workspace: Optional[torch.Tensor] =
         workspace = new_workspace(desc, parent_idx.device)
     hta_ancestor_masks(desc, parent_idx, masks, workspace, stream)
     return masks
+
+
+def rope_tree(q, k_tree, parent_idx, prefix_len, rope_theta: float, *, interleaved: bool = False,
+              max_prefix_len: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """Rotate q [B,T,Hq,D] and k_tree [B,Hkv,T,D] in place at positions prefix_len + depth;
+    returns the positions int32 [B, T].  max_prefix_len bounds the valid prefix_len values
+    (default: no bound below 2^31 - 1 - T)."""
+    B, T, Hq, D = q.shape
+    Hkv = k_tree.shape[1]
+    Lmax = (2 ** 31 - 1 - T) if max_prefix_len is None else int(max_prefix_len)
+    desc = make_desc(B, Hq, Hkv, D, T, 0, _dtype_code(q))
+    desc.max_prefix_len = Lmax
+    positions = torch.empty(B, T, dtype=torch.int32, device=q.device)
+    if workspace is None:
+        ws_desc = make_desc(B, Hq, Hkv, D, T, 0, _dtype_code(q))
+        workspace = new_workspace(ws_desc, q.device)
+    hta_rope_tree(desc, rope_theta, interleaved, q, k_tree, parent_idx, prefix_len, positions,
+                  workspace, stream)
+    return positions
+
+
+def accept_commit(logits, tokens, root_token, parent_idx, prefix_len, k_prefix, v_prefix,
+                  k_tree, v_tree, *, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Greedy acceptance along the draft trees and KV commit of the accepted paths (in place
+    on k_prefix, v_prefix, prefix_len).  Returns (target_next [B,T], accept_len [B],
+    accepted [B,T], bonus_token [B]), int32."""
+    B, Hkv, Lmax, D = k_prefix.shape
+    T = tokens.shape[1]
+    desc = make_desc(B, Hkv, Hkv, D, T, Lmax, _dtype_code(k_prefix))
+    dev = logits.device
+    target_next = torch.empty(B, T, dtype=torch.int32, device=dev)
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    accepted = torch.empty(B, T, dtype=torch.int32, device=dev)
+    bonus = torch.empty(B, dtype=torch.int32, device=dev)
+    if workspace is None:
+        n = accept_workspace_size(desc, logits.shape[-1])
+        if n == 0:
+            _check(2, "hta_accept_workspace_size")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    hta_accept_commit(desc, logits, tokens, root_token, parent_idx, prefix_len, k_prefix,
+                      v_prefix, k_tree, v_tree, target_next, accept_len, accepted, bonus,
+                      workspace, stream)
+    return target_next, accept_len, accepted, bonus
 
 
 def partial_views(desc: hta_desc, workspace: torch.Tensor):

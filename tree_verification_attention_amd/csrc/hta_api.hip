@@ -228,6 +228,82 @@ hta_status hta_merge(const hta_desc* desc, const int32_t* prefix_len, int32_t in
                                           (hipStream_t)stream));
 }
 
+hta_status hta_rope_tree(const hta_desc* desc, double rope_theta, int32_t interleaved, void* q,
+                         void* k_tree, const int32_t* parent_idx, const int32_t* prefix_len,
+                         int32_t* positions, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  Geometry G;
+  hta_plan_info p;
+  HTA_TRY(make_plan(desc, &G, &p));
+  if (!(rope_theta > 0.0) || isinf(rope_theta)) return HTA_ERR_SHAPE;
+  HTA_TRY(check_ptrs({q, k_tree, parent_idx, prefix_len}));
+  if (positions && !aligned16(positions)) return HTA_ERR_ALIGN;
+  // only the status words are written: any buffer past them will do
+  if (!workspace || workspace_bytes < p.masks_offset) return HTA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return HTA_ERR_ALIGN;
+  const Workspace ws = carve(workspace, p);
+  return hip_status(hta::launch_rope_tree(G, rope_theta, interleaved != 0, q, k_tree, parent_idx,
+                                          prefix_len, positions, ws.status,
+                                          (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// The accept workspace: the verify workspace, then the argmax span keys.
+hta_status accept_plan(const hta_desc* desc, int32_t vocab, int32_t logits_dtype, Geometry* g,
+                       hta_plan_info* p, size_t* keys_offset, size_t* total) {
+  HTA_TRY(make_plan(desc, g, p));
+  if (logits_dtype != HTA_BF16 && logits_dtype != HTA_F32) return HTA_ERR_DTYPE;
+  if (vocab < 1) return HTA_ERR_SHAPE;
+  int32_t span, nsplit;
+  hta::argmax_plan(vocab, logits_dtype == HTA_F32, &span, &nsplit);
+  *keys_offset = p->workspace_bytes;
+  *total = round_up(*keys_offset + sizeof(uint64_t) * (size_t)g->B * g->T * nsplit, 256);
+  return HTA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hta_accept_workspace_size(const hta_desc* desc, int32_t vocab) {
+  // sized for either logits dtype (fp32 logits take more, shorter spans per row)
+  Geometry G;
+  hta_plan_info p;
+  size_t off, total;
+  if (accept_plan(desc, vocab, HTA_BF16, &G, &p, &off, &total) != HTA_OK) return 0;
+  size_t off32, total32;
+  if (accept_plan(desc, vocab, HTA_F32, &G, &p, &off32, &total32) != HTA_OK) return 0;
+  return total > total32 ? total : total32;
+}
+
+hta_status hta_accept_commit(const hta_desc* desc, int32_t vocab, int32_t logits_dtype,
+                             const void* logits, const int32_t* tokens,
+                             const int32_t* root_token, const int32_t* parent_idx,
+                             int32_t* prefix_len, void* k_prefix, void* v_prefix,
+                             const void* k_tree, const void* v_tree, int32_t* target_next,
+                             int32_t* accept_len, int32_t* accepted, int32_t* bonus_token,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry G;
+  hta_plan_info p;
+  size_t keys_offset, total;
+  HTA_TRY(accept_plan(desc, vocab, logits_dtype, &G, &p, &keys_offset, &total));
+  if (!logits) return HTA_ERR_NULL;
+  HTA_TRY(check_ptrs({tokens, root_token, parent_idx, prefix_len, k_tree, v_tree, target_next,
+                      accept_len, accepted, bonus_token}));
+  if (G.Lmax > 0) HTA_TRY(check_ptrs({k_prefix, v_prefix}));
+  if (!workspace || workspace_bytes < total) return HTA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return HTA_ERR_ALIGN;
+  const Workspace ws = carve(workspace, p);
+  uint64_t* keys = (uint64_t*)((char*)workspace + keys_offset);
+  return hip_status(hta::launch_accept_commit(
+      G, vocab, logits_dtype == HTA_F32, logits, tokens, root_token, parent_idx, prefix_len,
+      k_prefix, v_prefix, k_tree, v_tree, target_next, accept_len, accepted, bonus_token,
+      ws.status, keys, (hipStream_t)stream));
+}
+
 hta_status hta_get_device_status(const hta_desc* desc, const void* workspace, void* stream,
                                  int32_t* bad_sequence) {
   Geometry G;
@@ -237,8 +313,8 @@ hta_status hta_get_device_status(const hta_desc* desc, const void* workspace, vo
   if (!workspace) return HTA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   int32_t host_status[1024];
-  hta_status first_tree = HTA_OK, first_len = HTA_OK;
-  int32_t bad_tree = -1, bad_len = -1;
+  hta_status first_tree = HTA_OK, first_len = HTA_OK, first_full = HTA_OK;
+  int32_t bad_tree = -1, bad_len = -1, bad_full = -1;
   for (int b0 = 0; b0 < G.B; b0 += 1024) {
     const int n = G.B - b0 < 1024 ? G.B - b0 : 1024;
     const char* src = (const char*)workspace + p.status_offset + sizeof(int32_t) * (size_t)b0;
@@ -255,6 +331,10 @@ hta_status hta_get_device_status(const hta_desc* desc, const void* workspace, vo
         first_len = HTA_ERR_PREFIX_LEN;
         bad_len = b0 + k;
       }
+      if ((host_status[k] & hta::kStatusCacheFull) && first_full == HTA_OK) {
+        first_full = HTA_ERR_CACHE_FULL;
+        bad_full = b0 + k;
+      }
     }
   }
   if (first_tree != HTA_OK) {
@@ -264,6 +344,10 @@ hta_status hta_get_device_status(const hta_desc* desc, const void* workspace, vo
   if (first_len != HTA_OK) {
     if (bad_sequence) *bad_sequence = bad_len;
     return first_len;
+  }
+  if (first_full != HTA_OK) {
+    if (bad_sequence) *bad_sequence = bad_full;
+    return first_full;
   }
   return HTA_OK;
 }
@@ -279,10 +363,12 @@ const char* hta_status_str(hta_status status) {
     case HTA_ERR_TREE: return "HTA_ERR_TREE: a parent pointer lies outside [-1, i-1]";
     case HTA_ERR_PREFIX_LEN: return "HTA_ERR_PREFIX_LEN: prefix_len outside [0, max_prefix_len]";
     case HTA_ERR_HIP: return "HTA_ERR_HIP: a HIP runtime call failed";
+    case HTA_ERR_CACHE_FULL:
+      return "HTA_ERR_CACHE_FULL: the accepted path does not fit the prefix cache";
   }
   return "HTA_ERR_UNKNOWN";
 }
 
-int32_t hta_version(void) { return 100; }
+int32_t hta_version(void) { return 200; }
 
 }  // extern "C"

@@ -23,6 +23,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Device status codes, one int32 per sequence in the workspace.
 constexpr int32_t kStatusTree = 1;       // a parent pointer outside [-1, i-1]
 constexpr int32_t kStatusPrefixLen = 2;  // prefix_len[b] outside [0, Lmax]
+constexpr int32_t kStatusCacheFull = 4;  // the accepted path does not fit the prefix cache
 
 // Geometry shared by every kernel of one call (a plain struct passed by value).
 struct Geometry {
@@ -116,6 +117,22 @@ hipError_t launch_tree_chain(const Geometry& g, const void* q, const void* k_tre
 hipError_t launch_prefix_attn_f32(const Geometry& g, const void* q, const void* k_prefix,
                                   const void* v_prefix, const int32_t* prefix_len,
                                   const Workspace& ws, hipStream_t stream);
+
+// Rotary encoding of the tree's q and k_tree rows in place at positions prefix_len + depth.
+hipError_t launch_rope_tree(const Geometry& g, double theta, bool interleaved, void* q,
+                            void* k_tree, const int32_t* parent_idx, const int32_t* prefix_len,
+                            int32_t* positions, int32_t* status, hipStream_t stream);
+// Span of logits each argmax workgroup scans, and the number of spans per row.
+void argmax_plan(int32_t vocab, bool f32, int32_t* span, int32_t* nsplit);
+// The target's greedy tokens (span keys in keys[B*T, nsplit]), greedy acceptance, KV commit:
+// two launches.
+hipError_t launch_accept_commit(const Geometry& g, int32_t vocab, bool logits_f32,
+                                const void* logits, const int32_t* tokens,
+                                const int32_t* root_token, const int32_t* parent_idx,
+                                int32_t* prefix_len, void* k_prefix, void* v_prefix,
+                                const void* k_tree, const void* v_tree, int32_t* target_next,
+                                int32_t* accept_len, int32_t* accepted, int32_t* bonus,
+                                int32_t* status, uint64_t* keys, hipStream_t stream);
 
 // How the prefix pass blocks the query rows of one KV head: mt full row tiles per wave,
 // tiles_per_block row tiles per workgroup, blocks workgroups per (sequence, KV head, chunk).
