@@ -233,6 +233,91 @@ def measured_peaks(dev) -> dict:
             "how": "512 MiB device copy (bytes read + written); 8192^3 bf16 torch.matmul"}
 
 
+def around_figures(name: str):
+    """Vocabulary and rotary base of the checkpoint a workload stands for."""
+    if name.startswith("vicuna"):
+        return W.VICUNA_VOCAB, W.VICUNA_ROPE_THETA
+    if name.startswith("qwq"):
+        return W.QWQ_VOCAB, W.QWQ_ROPE_THETA
+    return W.LLAMA3_VOCAB, W.LLAMA3_ROPE_THETA
+
+
+def bench_around(w: W.Workload, dev, stream, steps: int, warmup: int) -> dict:
+    """The steps on either side of the attention, timed with HIP events on the launch
+    stream: rotary encoding of the tree (hta_rope_tree), then the target's greedy tokens,
+    acceptance and KV commit (hta_accept_commit: the argmax launch and the acceptance
+    launch).  The caches grow by the accepted path on every call, as in decoding."""
+    vocab, theta = around_figures(w.name)
+    B, T, Hq, D = w.q.shape
+    Hkv = w.num_kv_heads
+    st = W.make_step_inputs(w.parent_idx.tolist(), vocab, dtype=torch.bfloat16, seed=w.seed + 7)
+    calls = warmup + 2 * steps
+    depth = max(max(W.depths(p)) for p in w.parent_idx.tolist()) + 1
+    Lmax = w.max_prefix_len + calls * depth
+    q = w.q.to(dev)
+    kt, vt = w.k_tree.to(dev), w.v_tree.to(dev)
+    par = w.parent_idx.to(dev)
+    plen0 = w.prefix_len.to(dev)
+    kp = torch.empty(B, Hkv, Lmax, D, dtype=w.dtype, device=dev)
+    vp = torch.empty_like(kp)
+    logits, tok, root = st.logits.to(dev), st.tokens.to(dev), st.root_token.to(dev)
+    desc = hta.make_desc(B, Hq, Hkv, D, T, Lmax, hta.binding._dtype_code(w.q))
+    ws = torch.empty(hta.accept_workspace_size(desc, vocab), dtype=torch.uint8, device=dev)
+    plen = plen0.clone()
+    outs = [torch.empty(B, T, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+            torch.empty(B, T, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev)]
+
+    def rope():
+        hta.hta_rope_tree(desc, theta, False, q, kt, par, plen, None, ws, stream)
+
+    def accept():
+        hta.hta_accept_commit(desc, logits, tok, root, par, plen, kp, vp, kt, vt, *outs, ws,
+                              stream)
+
+    for _ in range(warmup):
+        rope()
+        accept()
+    torch.cuda.synchronize()
+    code, _ = hta.hta_get_device_status(desc, ws, stream)
+    if code != 0:
+        raise RuntimeError(f"device status {hta.status_str(code)}")
+    n_acc = outs[1].float().mean().item()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        rope()
+    e1.record(stream)
+    e1.synchronize()
+    rope_us = e0.elapsed_time(e1) / steps * 1e3
+    e0.record(stream)
+    for _ in range(steps):
+        accept()
+    e1.record(stream)
+    e1.synchronize()
+    accept_us = e0.elapsed_time(e1) / steps * 1e3
+    code, _ = hta.hta_get_device_status(desc, ws, stream)
+    if code != 0:
+        raise RuntimeError(f"device status {hta.status_str(code)}")
+    esz = w.q.element_size()
+    rope_bytes = 2 * (B * T * Hq * D + B * Hkv * T * D) * esz
+    logits_bytes = B * T * vocab * 2
+    log(f"[bench] rope_tree {rope_us:.2f} us; accept_commit (argmax + acceptance) "
+        f"{accept_us:.2f} us; {n_acc:.2f} nodes accepted per sequence")
+    return {
+        "vocab": vocab, "rope_theta": theta, "logits_dtype": "bf16",
+        "accepted_nodes_per_sequence": round(n_acc, 3),
+        "rope_tree_us": round(rope_us, 3),
+        "rope_tree_alg_bytes": rope_bytes,
+        "accept_commit_us": round(accept_us, 3),
+        "logits_bytes": logits_bytes,
+        "accept_commit_GBps": round(logits_bytes / (accept_us * 1e-6) / 1e9, 1),
+        "accept_commit_frac_of_hbm_peak": round(logits_bytes / (accept_us * 1e-6) / 1e9
+                                                / HBM_PEAK_GBS, 4),
+        "note": "accept_commit = the vocabulary argmax launch plus the acceptance/commit "
+                "launch; the kernel trace splits the two",
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -427,6 +512,7 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": round(achieved_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
         },
     }
+    result["around_attention"] = bench_around(w, dev, stream, args.steps, args.warmup)
     peaks = measured_peaks(dev)
     log(f"[bench] measured peaks: {peaks}")
     result["measured_peaks"] = peaks
