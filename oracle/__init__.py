@@ -60,6 +60,8 @@ def configure(L: ctypes.CDLL) -> ctypes.CDLL:
     L.hta_oracle_check_tree.argtypes = [i, i, P]
     L.hta_oracle_masked_attention.argtypes = [i, i, i, P, P, P, P, ctypes.c_double, P, P]
     L.hta_oracle_lse_merge.argtypes = [i, i, P, P, P, P]
+    L.hta_oracle_chunk_mass.argtypes = [i, i, i, i, i, i, i, P, P, P, P, P, ctypes.c_double,
+                                        i, i, i, P, P, P, P]
     L.step_oracle_depths.argtypes = [i, i, P, P]
     L.step_oracle_rope.argtypes = [i, i, i, i, i, i, P, P, P, ctypes.c_double, i, P, P]
     L.step_oracle_round_bf16.argtypes = [ctypes.c_size_t, P, P]
@@ -68,7 +70,7 @@ def configure(L: ctypes.CDLL) -> ctypes.CDLL:
     L.step_oracle_accept.argtypes = [i, i, P, P, P, P, P, P, P]
     for f in (L.hta_oracle_rows, L.hta_oracle_verify, L.hta_oracle_masks,
               L.hta_oracle_check_tree, L.hta_oracle_masked_attention, L.hta_oracle_lse_merge,
-              L.step_oracle_depths, L.step_oracle_rope, L.step_oracle_argmax,
+              L.hta_oracle_chunk_mass, L.step_oracle_depths, L.step_oracle_rope, L.step_oracle_argmax,
               L.step_oracle_accept):
         f.restype = ctypes.c_int
     return L
@@ -154,6 +156,25 @@ def rows(arrs: Dict[str, np.ndarray], scale: float, row_b: Sequence[int], row_h:
                                _ptr(out), _ptr(lse))
     _check(rc)
     return out, lse
+
+
+def chunk_mass(arrs: Dict[str, np.ndarray], scale: float, chunk: int, nchunks: int,
+               row_b: Sequence[int], row_h: Sequence[int], row_i: Sequence[int]) -> np.ndarray:
+    """Share of each selected row's attention on prefix chunk s (columns s < nchunks) and on
+    the tree (column nchunks): fp64 [n, nchunks + 1], rows summing to 1."""
+    a, (B, T, Hq, Hkv, D, Lmax) = _inputs(arrs)
+    rb = np.ascontiguousarray(row_b, dtype=np.int32)
+    rh = np.ascontiguousarray(row_h, dtype=np.int32)
+    ri = np.ascontiguousarray(row_i, dtype=np.int32)
+    n = rb.shape[0]
+    mass = np.empty((n, nchunks + 1), dtype=np.float64)
+    rc = lib().hta_oracle_chunk_mass(B, T, Hq, Hkv, D, Lmax, a["is_bf16"], _ptr(a["q"]),
+                                     _ptr(a["k_prefix"]), _ptr(a["k_tree"]),
+                                     _ptr(a["parent_idx"]), _ptr(a["prefix_len"]), float(scale),
+                                     int(chunk), int(nchunks), n, _ptr(rb), _ptr(rh), _ptr(ri),
+                                     _ptr(mass))
+    _check(rc)
+    return mass
 
 
 def ancestor_masks(parent_idx: np.ndarray) -> np.ndarray:

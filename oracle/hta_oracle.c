@@ -342,3 +342,83 @@ int hta_oracle_lse_merge(int nparts, int D, const double *lse_parts, const doubl
     *lse = M + log(W);
     return HTA_ORACLE_OK;
 }
+
+/*
+ * Attention mass per prefix chunk for an explicit list of rows (b, h, i).  With p_j the
+ * softmax weights of the row's full verification attention (over its visible prefix and
+ * tree keys, as above),
+ *   mass[r, s]       = sum of p_j over the prefix keys j in [s*chunk, (s+1)*chunk), s < nchunks
+ *   mass[r, nchunks] = sum of p_j over the row's visible tree keys
+ * so every row sums to 1.  This is each split-K chunk's share of the row's attention
+ * (LongSpec README, Introduction: the prefix part is computed chunk-parallel and aggregated
+ * through the partial log-sum-exps).  nchunks * chunk must cover Lmax.
+ */
+int hta_oracle_chunk_mass(int B, int T, int Hq, int Hkv, int D, int Lmax, int is_bf16,
+                          const void *q, const void *k_prefix, const void *k_tree,
+                          const int32_t *parent, const int32_t *prefix_len, double scale,
+                          int chunk, int nchunks, int nrows, const int32_t *row_b,
+                          const int32_t *row_h, const int32_t *row_i, double *mass)
+{
+    if (B <= 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Lmax < 0 || Hq % Hkv != 0 ||
+        chunk <= 0 || nchunks < 0 || (long long)nchunks * chunk < Lmax)
+        return HTA_ORACLE_BAD_ARG;
+    for (int b = 0; b < B; ++b) {
+        if (prefix_len[b] < 0 || prefix_len[b] > Lmax)
+            return HTA_ORACLE_BAD_ARG;
+        if (!tree_is_valid(parent + (size_t)b * T, T))
+            return HTA_ORACLE_BAD_TREE;
+    }
+    const int G = Hq / Hkv;
+    double *scores = (double *)malloc(((size_t)Lmax + (size_t)T) * sizeof(double));
+    unsigned char *in_tree = (unsigned char *)malloc((size_t)T);
+    if (!scores || !in_tree) {
+        free(scores); free(in_tree);
+        return HTA_ORACLE_NOMEM;
+    }
+    int rc = HTA_ORACLE_OK;
+    for (int r = 0; r < nrows; ++r) {
+        const int b = row_b[r], h = row_h[r], i = row_i[r];
+        if (b < 0 || b >= B || h < 0 || h >= Hq || i < 0 || i >= T) {
+            rc = HTA_ORACLE_BAD_ARG;
+            break;
+        }
+        const int g = h / G, L = prefix_len[b];
+        const size_t qoff = (((size_t)b * T + i) * Hq + h) * D;
+        const size_t pbase = ((size_t)b * Hkv + g) * (size_t)Lmax * D;
+        const size_t tbase = ((size_t)b * Hkv + g) * (size_t)T * D;
+        const int32_t *par = parent + (size_t)b * T;
+        memset(in_tree, 0, (size_t)T);
+        for (int p = i; p != -1; p = par[p])
+            in_tree[p] = 1;
+        /* scores of the visible keys: prefix keys 0..L-1, then tree keys t (in_tree[t]) */
+        double m = -INFINITY;
+        for (int j = 0; j < L + T; ++j) {
+            if (j >= L && !in_tree[j - L])
+                continue;
+            double s = 0.0;
+            for (int d = 0; d < D; ++d) {
+                const double kd = j < L ? widen(k_prefix, pbase + (size_t)j * D + d, is_bf16)
+                                        : widen(k_tree, tbase + (size_t)(j - L) * D + d, is_bf16);
+                s += widen(q, qoff + d, is_bf16) * kd;
+            }
+            scores[j] = s * scale;
+            if (scores[j] > m)
+                m = scores[j];
+        }
+        double Z = 0.0;
+        for (int j = 0; j < L + T; ++j)
+            if (j < L || in_tree[j - L])
+                Z += exp(scores[j] - m);
+        double *row = mass + (size_t)r * (nchunks + 1);
+        for (int s = 0; s <= nchunks; ++s)
+            row[s] = 0.0;
+        for (int j = 0; j < L + T; ++j) {
+            if (j >= L && !in_tree[j - L])
+                continue;
+            const int bin = j < L ? j / chunk : nchunks;
+            row[bin] += exp(scores[j] - m) / Z;
+        }
+    }
+    free(scores); free(in_tree);
+    return rc;
+}
