@@ -512,6 +512,23 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": round(achieved_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
         },
     }
+    # ---- each chunk's share of every row's attention, from the partials the steps left
+    mass = torch.empty(B, Hq, T, info.num_splits + 1, dtype=torch.float32, device=dev)
+    scores = torch.empty(B, info.num_splits + 1, dtype=torch.float32, device=dev)
+    step(0)
+    for _ in range(50):
+        hta.hta_chunk_mass(desc, plen, lse, mass, scores, ws, stream)
+    e0.record(stream)
+    for _ in range(args.steps):
+        hta.hta_chunk_mass(desc, plen, lse, mass, scores, ws, stream)
+    e1.record(stream)
+    e1.synchronize()
+    mass_us = e0.elapsed_time(e1) / args.steps * 1e3
+    log(f"[bench] chunk_mass: {mass_us:.2f} us")
+    result["chunk_mass"] = {
+        "us": round(mass_us, 3), "columns": info.num_splits + 1,
+        "bytes": int((mass.numel() * 2 + lse.numel() * (info.num_splits + 1)) * 4),
+    }
     result["around_attention"] = bench_around(w, dev, stream, args.steps, args.warmup)
     peaks = measured_peaks(dev)
     log(f"[bench] measured peaks: {peaks}")

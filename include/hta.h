@@ -126,7 +126,9 @@ size_t hta_workspace_size(const hta_desc *desc);
  * abstract).  Two launches: the prefix pass, and a merge that computes each row's tree
  * attention over its node's parent chain itself (validating the trees and recording the
  * device status) instead of reading a tree partial; the ancestor masks are not materialised
- * here (hta_ancestor_masks builds them).  The workspace partial buffers are overwritten.
+ * here (hta_ancestor_masks builds them).  The workspace partial buffers are overwritten:
+ * the prefix slots with the prefix partials, the tree slot's lse_part with the tree part's
+ * log-sum-exp (its o_part row is left as it was).
  */
 hta_status hta_verify(const hta_desc *desc, const void *q, const void *k_prefix,
                       const void *v_prefix, const void *k_tree, const void *v_tree,
@@ -171,6 +173,27 @@ hta_status hta_tree_partials(const hta_desc *desc, const void *q, const void *k_
 hta_status hta_merge(const hta_desc *desc, const int32_t *prefix_len, int32_t include_tree,
                      float *out, float *lse, void *workspace, size_t workspace_bytes,
                      void *stream);
+
+/*
+ * Each prefix chunk's share of every query row's attention, and the tree's: the split-K
+ * partial log-sum-exps of the last hta_verify call on this workspace (or of
+ * hta_prefix_partials + hta_tree_partials) against the rows' final lse from that call
+ * (README, Introduction: the prefix is attended chunk by chunk and aggregated through
+ * these statistics):
+ *     mass[b, h, i, s] = exp(lse_part[b, g, s, r] - lse[b, h, i])     s <= num_splits
+ * with g, r the row's KV head and packed row (hta_plan_info), column s < num_splits the
+ * prefix keys [s*chunk, (s+1)*chunk) (0 for chunks past prefix_len[b]) and column
+ * num_splits the tree; every row sums to 1 up to rounding.  mass is float
+ * [B, Hq, T, num_splits + 1] (device).  chunk_scores (device float [B, num_splits + 1], may
+ * be NULL) receives each column's mean over the sequence's Hq * T rows, summed in a fixed
+ * order (bitwise reproducible): the attention each prefix chunk received, e.g. to choose
+ * the context a drafter keeps.  The chunk length is the plan's (set desc->chunk to choose
+ * the granularity; it must be the one the partials were computed with).  Rows of a
+ * sequence that hta_verify rejected are NaN.  batch <= 65535.
+ */
+hta_status hta_chunk_mass(const hta_desc *desc, const int32_t *prefix_len, const float *lse,
+                          float *mass, float *chunk_scores, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 /*
  * ---- The steps on either side of the attention in one greedy verification step ----

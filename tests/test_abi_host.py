@@ -247,3 +247,18 @@ def test_accept_commit_validates_before_launching():
     assert code(ws=None) == WORKSPACE
     assert code(ws=FAKE + 64) == ALIGN
     assert code(desc=_desc(num_q_heads=30)) == SHAPE
+
+
+def test_chunk_mass_validates_before_launching():
+    L = hta.load()
+    d = _desc()
+    n = hta.workspace_size(d)
+    call = lambda *p, nbytes=n, desc=d: L.hta_chunk_mass(ctypes.byref(desc), *p, nbytes, None)  # noqa: E731
+    assert call(None, FAKE, FAKE, FAKE, FAKE) == NULL
+    assert call(FAKE, None, FAKE, FAKE, FAKE) == NULL
+    assert call(FAKE, FAKE, None, FAKE, FAKE) == NULL
+    assert call(FAKE, FAKE, FAKE + 4, FAKE, FAKE) == ALIGN
+    assert call(FAKE, FAKE, FAKE, FAKE + 4, FAKE) == ALIGN
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, nbytes=n - 1) == WORKSPACE
+    assert call(FAKE, FAKE, FAKE, FAKE, None) == WORKSPACE
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, desc=_desc(head_dim=80)) == SHAPE

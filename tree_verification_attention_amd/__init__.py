@@ -11,9 +11,11 @@ from .binding import (  # noqa: F401
     accept_commit,
     accept_workspace_size,
     ancestor_masks,
+    chunk_mass,
     desc_for,
     hta_accept_commit,
     hta_ancestor_masks,
+    hta_chunk_mass,
     hta_get_device_status,
     hta_merge,
     hta_prefix_partials,
@@ -32,8 +34,8 @@ from .binding import (  # noqa: F401
 )
 
 __all__ = [
-    "HtaError", "accept_commit", "accept_workspace_size", "ancestor_masks", "desc_for",
-    "hta_accept_commit", "hta_ancestor_masks", "hta_get_device_status", "hta_merge",
+    "HtaError", "accept_commit", "accept_workspace_size", "ancestor_masks", "chunk_mass",
+    "desc_for", "hta_accept_commit", "hta_ancestor_masks", "hta_chunk_mass", "hta_get_device_status", "hta_merge",
     "hta_prefix_partials", "hta_rope_tree", "hta_tree_partials", "hta_verify", "load",
     "make_desc", "new_workspace", "partial_views", "plan", "rope_tree", "status_str", "verify",
     "workspace_size",

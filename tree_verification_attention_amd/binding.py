@@ -38,6 +38,7 @@ EXPORTED = (
     "hta_tree_partials",
     "hta_merge",
     "hta_get_device_status",
+    "hta_chunk_mass",
     "hta_rope_tree",
     "hta_accept_workspace_size",
     "hta_accept_commit",
@@ -106,6 +107,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.hta_merge.argtypes = [D, P, I, P, P, P, S, P]
     L.hta_get_device_status.argtypes = [D, P, P, ctypes.POINTER(ctypes.c_int32)]
     L.hta_rope_tree.argtypes = [D, ctypes.c_double, I, P, P, P, P, P, P, S, P]
+    L.hta_chunk_mass.argtypes = [D, P, P, P, P, P, S, P]
     L.hta_accept_workspace_size.argtypes = [D, I]
     L.hta_accept_workspace_size.restype = S
     L.hta_accept_commit.argtypes = [D, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
@@ -114,7 +116,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.hta_version.argtypes = []
     for f in (L.hta_plan, L.hta_verify, L.hta_ancestor_masks, L.hta_prefix_partials,
               L.hta_tree_partials, L.hta_merge, L.hta_get_device_status, L.hta_version,
-              L.hta_rope_tree, L.hta_accept_commit):
+              L.hta_rope_tree, L.hta_accept_commit, L.hta_chunk_mass):
         f.restype = ctypes.c_int
     _lib = L
     return L
@@ -232,6 +234,26 @@ def hta_get_device_status(desc, workspace, stream=None) -> Tuple[int, int]:
     code = load().hta_get_device_status(ctypes.byref(desc), _ptr(workspace), _stream(stream),
                                         ctypes.byref(bad))
     return int(code), int(bad.value)
+
+
+def hta_chunk_mass(desc, prefix_len, lse, mass, chunk_scores, workspace, stream=None) -> None:
+    _contig(prefix_len, lse, mass, workspace)
+    if chunk_scores is not None:
+        _contig(chunk_scores)
+    _check(load().hta_chunk_mass(ctypes.byref(desc), _ptr(prefix_len), _ptr(lse), _ptr(mass),
+                                 _ptr(chunk_scores), _ptr(workspace), workspace.numel(),
+                                 _stream(stream)), "hta_chunk_mass")
+
+
+def chunk_mass(desc, prefix_len, lse, workspace, stream=None):
+    """Each chunk's share of every query row's attention after hta_verify on this workspace:
+    (mass float [B, Hq, T, S+1], chunk_scores float [B, S+1]); column S is the tree."""
+    p = plan(desc)
+    B, Hq, T = desc.batch, desc.num_q_heads, desc.tree_size
+    mass = torch.empty(B, Hq, T, p.num_splits + 1, dtype=torch.float32, device=lse.device)
+    scores = torch.empty(B, p.num_splits + 1, dtype=torch.float32, device=lse.device)
+    hta_chunk_mass(desc, prefix_len, lse, mass, scores, workspace, stream)
+    return mass, scores
 
 
 def hta_rope_tree(desc, rope_theta: float, interleaved: bool, q, k_tree, parent_idx, prefix_len,

@@ -247,6 +247,21 @@ hta_status hta_rope_tree(const hta_desc* desc, double rope_theta, int32_t interl
                                           (hipStream_t)stream));
 }
 
+hta_status hta_chunk_mass(const hta_desc* desc, const int32_t* prefix_len, const float* lse,
+                          float* mass, float* chunk_scores, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  Geometry G;
+  hta_plan_info p;
+  HTA_TRY(make_plan(desc, &G, &p));
+  HTA_TRY(check_ptrs({prefix_len, lse, mass}));
+  if (chunk_scores && !aligned16(chunk_scores)) return HTA_ERR_ALIGN;
+  if ((size_t)G.B > 65535) return HTA_ERR_SHAPE;
+  HTA_TRY(check_ws(p, workspace, workspace_bytes));
+  const Workspace ws = carve(workspace, p);
+  return hip_status(hta::launch_chunk_mass(G, prefix_len, lse, mass, chunk_scores, ws,
+                                           (hipStream_t)stream));
+}
+
 }  // extern "C"
 
 namespace {

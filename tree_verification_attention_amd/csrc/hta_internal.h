@@ -134,6 +134,12 @@ hipError_t launch_accept_commit(const Geometry& g, int32_t vocab, bool logits_f3
                                 int32_t* accept_len, int32_t* accepted, int32_t* bonus,
                                 int32_t* status, uint64_t* keys, hipStream_t stream);
 
+// Each chunk's (and the tree's) share of every query row's attention from the partial
+// log-sum-exps in the workspace and the rows' final log-sum-exps; optional per-sequence means.
+hipError_t launch_chunk_mass(const Geometry& g, const int32_t* prefix_len, const float* lse,
+                             float* mass, float* scores, const Workspace& ws,
+                             hipStream_t stream);
+
 // How the prefix pass blocks the query rows of one KV head: mt full row tiles per wave,
 // tiles_per_block row tiles per workgroup, blocks workgroups per (sequence, KV head, chunk).
 void prefix_row_blocking(const Geometry& g, int* mt, int* tiles_per_block, int* blocks);

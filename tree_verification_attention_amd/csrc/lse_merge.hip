@@ -312,7 +312,11 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   float ltot = 0.f;
   if constexpr (FUSED) {
     ltot = group_sum4(lt);                         // the tree's weight sum relative to mt
-    Mn = fmaxf(Mn, (mt + __log2f(ltot)) * kLn2);  // the tree part's log-sum-exp
+    const float lse_tree_nat = (mt + __log2f(ltot)) * kLn2;  // the tree part's log-sum-exp
+    Mn = fmaxf(Mn, lse_tree_nat);
+    // kept in the tree slot of lse_part (its o_part row is not written): with the prefix
+    // slots it gives every chunk's share of the row's attention
+    if (lane == 0) a.lse_part[(base + G.S) * G.R_pad + r] = lse_tree_nat;
   }
   const float M = Mn * kLog2e;  // the same maximum in log2 units
   if (Mn == -INFINITY) {  // no visible key at all (prefix-only merge of an empty prefix)
