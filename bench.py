@@ -529,6 +529,35 @@ def main() -> int:
         "us": round(mass_us, 3), "columns": info.num_splits + 1,
         "bytes": int((mass.numel() * 2 + lse.numel() * (info.num_splits + 1)) * 4),
     }
+    # ---- the method's "before": one masked pass over all L + T keys, explicit mask
+    dmask = torch.empty(hta.dense_mask_shape(desc), dtype=torch.int64, device=dev)
+    hta.hta_dense_mask(desc, par, plen, dmask, ws, stream)
+    dense_steps = max(20, args.steps // 5)
+    for k in range(20):
+        hta.hta_verify_dense(desc, q, kps[k % n_copies], vps[k % n_copies], kt, vt, dmask, plen,
+                             out, lse, stream)
+    e0.record(stream)
+    for k in range(dense_steps):
+        hta.hta_verify_dense(desc, q, kps[k % n_copies], vps[k % n_copies], kt, vt, dmask, plen,
+                             out, lse, stream)
+    e1.record(stream)
+    e1.synchronize()
+    dense_us = e0.elapsed_time(e1) / dense_steps * 1e3
+    e0.record(stream)
+    for _ in range(dense_steps):
+        hta.hta_dense_mask(desc, par, plen, dmask, ws, stream)
+    e1.record(stream)
+    e1.synchronize()
+    dmask_us = e0.elapsed_time(e1) / dense_steps * 1e3
+    log(f"[bench] single-pass masked baseline: {dense_us:.1f} us (+ mask {dmask_us:.1f} us), "
+        f"{(dense_us + dmask_us) / step_events_us:.2f}x the hybrid step")
+    result["dense_masked_baseline"] = {
+        "us": round(dense_us, 3), "mask_build_us": round(dmask_us, 3),
+        "mask_bytes": int(dmask.numel() * 8), "launches_timed": dense_steps,
+        "before_over_after": round((dense_us + dmask_us) / step_events_us, 3),
+        "note": "one masked pass over all L+T keys per (64 query rows, KV head), explicit "
+                "mask; before_over_after = (mask build + pass) / the hybrid step (HIP events)",
+    }
     result["around_attention"] = bench_around(w, dev, stream, args.steps, args.warmup)
     peaks = measured_peaks(dev)
     log(f"[bench] measured peaks: {peaks}")

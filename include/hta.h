@@ -196,6 +196,49 @@ hta_status hta_chunk_mass(const hta_desc *desc, const int32_t *prefix_len, const
                           size_t workspace_bytes, void *stream);
 
 /*
+ * ---- Verification without the hybrid split: the method's "before" ----
+ *
+ * The paper summary (Summary; Key points, "Hybrid Tree Attention") says a tree mask keeps
+ * verification off the optimized long-context attention kernels and that the hybrid split
+ * cut the target's attention latency to about a quarter.  These two calls are that "before"
+ * on this hardware: an explicit mask over all L + T keys of every node, and one masked
+ * attention pass over them (parallel over query tiles and KV heads, every workgroup
+ * streaming the whole key range of its KV head; no split over keys, no merge).  Same
+ * result as hta_verify (up to rounding) when the mask is the one hta_dense_mask builds.
+ *
+ * Mask layout (word-major): uint64 [B, W, T_pad] with W = ceil(Lmax/64) + ceil(T/64) words
+ * per node and T_pad = T rounded up to even; word w of node i of sequence b is element
+ * (b, w, i).  Bit j % 64 of word j / 64 is prefix key j; bit t % 64 of word
+ * ceil(Lmax/64) + t / 64 is tree key t.  (Word-major, so the words one key tile needs for
+ * consecutive nodes are contiguous.)
+ */
+
+/* Bytes of the explicit mask, 8 * B * W * T_pad (0 for an invalid descriptor). */
+size_t hta_dense_mask_bytes(const hta_desc *desc);
+
+/*
+ * Build the explicit mask of every node: prefix keys j < prefix_len[b] and the node's
+ * ancestors-or-self in the tree.  An invalid tree or prefix_len leaves that sequence's mask
+ * all zero (its rows then see nothing: out 0, lse -inf) and is recorded in the workspace
+ * status (any buffer of at least 4 * batch bytes rounded up to 256).  The padding column of
+ * an odd T is written as zero.
+ */
+hta_status hta_dense_mask(const hta_desc *desc, const int32_t *parent_idx,
+                          const int32_t *prefix_len, uint64_t *mask, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
+ * Single-pass masked attention over all L + T keys: key j < prefix_len[b] of the prefix or
+ * tree key t is visible to node i iff its mask bit is set.  out, lse as for hta_verify (a
+ * row that sees no key gets out 0, lse -inf; a prefix_len outside [0, Lmax] gives NaN).
+ * bf16 inputs only.  No workspace.
+ */
+hta_status hta_verify_dense(const hta_desc *desc, const void *q, const void *k_prefix,
+                            const void *v_prefix, const void *k_tree, const void *v_tree,
+                            const uint64_t *mask, const int32_t *prefix_len, float *out,
+                            float *lse, void *stream);
+
+/*
  * ---- The steps on either side of the attention in one greedy verification step ----
  *
  * Speculative decoding at temperature 0 (LongSpec README, Evaluation: both inference

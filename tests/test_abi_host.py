@@ -262,3 +262,25 @@ def test_chunk_mass_validates_before_launching():
     assert call(FAKE, FAKE, FAKE, FAKE, FAKE, nbytes=n - 1) == WORKSPACE
     assert call(FAKE, FAKE, FAKE, FAKE, None) == WORKSPACE
     assert call(FAKE, FAKE, FAKE, FAKE, FAKE, desc=_desc(head_dim=80)) == SHAPE
+
+
+def test_dense_mask_bytes_and_validation():
+    L = hta.load()
+    d = _desc()  # Lmax 32768, T 68: 512 + 2 words per node, T_pad 68
+    assert hta.load().hta_dense_mask_bytes(ctypes.byref(d)) == 8 * 1 * 514 * 68
+    d7 = _desc(tree_size=7, max_prefix_len=100)  # 2 + 1 words, T_pad 8
+    assert hta.load().hta_dense_mask_bytes(ctypes.byref(d7)) == 8 * 3 * 8
+    assert hta.load().hta_dense_mask_bytes(ctypes.byref(_desc(head_dim=80))) == 0
+    assert B.dense_mask_shape(d7) == (1, 3, 8)
+    assert L.hta_dense_mask(ctypes.byref(d), None, FAKE, FAKE, FAKE, 256, None) == NULL
+    assert L.hta_dense_mask(ctypes.byref(d), FAKE, FAKE, FAKE + 8, FAKE, 256, None) == ALIGN
+    assert L.hta_dense_mask(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 255, None) == WORKSPACE
+    p = [FAKE] * 9  # q, k/v_prefix, k/v_tree, mask, prefix_len, out, lse (never launched)
+    for i in (0, 3, 4, 5, 6, 7, 8):
+        q = list(p)
+        q[i] = None
+        assert L.hta_verify_dense(ctypes.byref(d), *q, None) == NULL, i
+    q = list(p)
+    q[5] = FAKE + 8
+    assert L.hta_verify_dense(ctypes.byref(d), *q, None) == ALIGN
+    assert L.hta_verify_dense(ctypes.byref(_desc(in_dtype=1)), *p, None) == DTYPE

@@ -46,6 +46,8 @@ MUTANTS = {
                               "    *lse = m + log(Z);\n}"),
     "exp_sign": ("double p = exp(scores[j] - m);\n        Z += p;\n        for (int d = 0; d < D; ++d)\n            out[d] += p * widen",
                  "double p = exp(scores[j] + m);\n        Z += p;\n        for (int d = 0; d < D; ++d)\n            out[d] += p * widen"),
+    "masked_attention_mask_ignored": ("            if (!mask[(size_t)i * nk + j])\n                continue;\n            double s = 0.0;",
+                                      "            double s = 0.0;"),
     "tree_keys_wrong_head": ("const size_t base = ((size_t)b * Hkv + g) * (size_t)T * D;",
                              "const size_t base = ((size_t)b * Hkv + 0) * (size_t)T * D;"),
 }
@@ -109,6 +111,11 @@ def _mask_pin():
         assert full == (1 << (i + 1)) - 1
 
 
+def _masked_attention_pin():
+    from test_oracle_pins import test_masked_attention_matches_fp64_sdpa_with_a_boolean_mask
+    test_masked_attention_matches_fp64_sdpa_with_a_boolean_mask()
+
+
 def _merge_pin():
     rng = np.random.default_rng(1)
     q = rng.standard_normal((1, 4))
@@ -126,7 +133,8 @@ def _merge_pin():
     assert abs(l - l_ref[0]) < 1e-12
 
 
-PINS = [_bruteforce_pin, _causal_pin, _closed_form_pin, _mask_pin, _merge_pin]
+PINS = [_bruteforce_pin, _causal_pin, _closed_form_pin, _mask_pin, _merge_pin,
+        _masked_attention_pin]
 
 
 def test_pins_pass_on_the_real_oracle():

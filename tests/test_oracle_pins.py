@@ -384,3 +384,34 @@ def test_invalid_trees_are_rejected(bad):
     a["parent_idx"] = par
     with pytest.raises(oracle.OracleError):
         oracle.verify(a, 1.0)
+
+
+# ----------------------------------------------------------------------------- general masked attention
+
+
+def test_masked_attention_matches_fp64_sdpa_with_a_boolean_mask():
+    """The general masked-attention oracle against torch's fp64 scaled_dot_product_attention
+    with a boolean mask and against logsumexp of the masked scores; an all-masked row gives
+    out 0, lse -inf."""
+    rng = np.random.default_rng(40)
+    nq, nk, D, scale = 9, 37, 12, 0.37
+    q = rng.standard_normal((nq, D)) * 1.5
+    k = rng.standard_normal((nk, D))
+    v = rng.standard_normal((nk, D))
+    mask = rng.random((nq, nk)) < 0.4
+    mask[0, :] = False          # sees nothing
+    mask[1, :] = True           # sees everything
+    mask[2, :] = False
+    mask[2, 17] = True          # sees one key
+    out, lse = oracle.masked_attention(q, k, v, mask, scale)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    tm = torch.from_numpy(mask)
+    rows = np.nonzero(mask.any(axis=1))[0]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        tq[rows][None], tk[None], tv[None], attn_mask=tm[rows][None], scale=scale)[0].numpy()
+    np.testing.assert_allclose(out[rows], ref, rtol=0, atol=1e-13)
+    s = (tq @ tk.T) * scale
+    ref_lse = torch.logsumexp(s.masked_fill(~tm, float("-inf")), dim=1).numpy()
+    np.testing.assert_allclose(lse[rows], ref_lse[rows], rtol=0, atol=1e-13)
+    assert lse[0] == -np.inf and (out[0] == 0).all()
+    np.testing.assert_allclose(out[2], v[17], atol=1e-15)

@@ -12,16 +12,19 @@ from .binding import (  # noqa: F401
     accept_workspace_size,
     ancestor_masks,
     chunk_mass,
+    dense_mask_shape,
     desc_for,
     hta_accept_commit,
     hta_ancestor_masks,
     hta_chunk_mass,
+    hta_dense_mask,
     hta_get_device_status,
     hta_merge,
     hta_prefix_partials,
     hta_rope_tree,
     hta_tree_partials,
     hta_verify,
+    hta_verify_dense,
     load,
     make_desc,
     new_workspace,
@@ -30,12 +33,14 @@ from .binding import (  # noqa: F401
     rope_tree,
     status_str,
     verify,
+    verify_dense,
     workspace_size,
 )
 
 __all__ = [
     "HtaError", "accept_commit", "accept_workspace_size", "ancestor_masks", "chunk_mass",
-    "desc_for", "hta_accept_commit", "hta_ancestor_masks", "hta_chunk_mass", "hta_get_device_status", "hta_merge",
+    "dense_mask_shape", "desc_for", "hta_accept_commit", "hta_ancestor_masks", "hta_chunk_mass",
+    "hta_dense_mask", "hta_verify_dense", "verify_dense", "hta_get_device_status", "hta_merge",
     "hta_prefix_partials", "hta_rope_tree", "hta_tree_partials", "hta_verify", "load",
     "make_desc", "new_workspace", "partial_views", "plan", "rope_tree", "status_str", "verify",
     "workspace_size",

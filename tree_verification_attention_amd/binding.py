@@ -39,6 +39,9 @@ EXPORTED = (
     "hta_merge",
     "hta_get_device_status",
     "hta_chunk_mass",
+    "hta_dense_mask_bytes",
+    "hta_dense_mask",
+    "hta_verify_dense",
     "hta_rope_tree",
     "hta_accept_workspace_size",
     "hta_accept_commit",
@@ -108,6 +111,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.hta_get_device_status.argtypes = [D, P, P, ctypes.POINTER(ctypes.c_int32)]
     L.hta_rope_tree.argtypes = [D, ctypes.c_double, I, P, P, P, P, P, P, S, P]
     L.hta_chunk_mass.argtypes = [D, P, P, P, P, P, S, P]
+    L.hta_dense_mask_bytes.argtypes = [D]
+    L.hta_dense_mask_bytes.restype = S
+    L.hta_dense_mask.argtypes = [D, P, P, P, P, S, P]
+    L.hta_verify_dense.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
     L.hta_accept_workspace_size.argtypes = [D, I]
     L.hta_accept_workspace_size.restype = S
     L.hta_accept_commit.argtypes = [D, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
@@ -116,7 +123,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.hta_version.argtypes = []
     for f in (L.hta_plan, L.hta_verify, L.hta_ancestor_masks, L.hta_prefix_partials,
               L.hta_tree_partials, L.hta_merge, L.hta_get_device_status, L.hta_version,
-              L.hta_rope_tree, L.hta_accept_commit, L.hta_chunk_mass):
+              L.hta_rope_tree, L.hta_accept_commit, L.hta_chunk_mass, L.hta_dense_mask,
+              L.hta_verify_dense):
         f.restype = ctypes.c_int
     _lib = L
     return L
@@ -243,6 +251,48 @@ def hta_chunk_mass(desc, prefix_len, lse, mass, chunk_scores, workspace, stream=
     _check(load().hta_chunk_mass(ctypes.byref(desc), _ptr(prefix_len), _ptr(lse), _ptr(mass),
                                  _ptr(chunk_scores), _ptr(workspace), workspace.numel(),
                                  _stream(stream)), "hta_chunk_mass")
+
+
+def dense_mask_shape(desc: hta_desc) -> Tuple[int, int, int]:
+    """(B, W, T_pad) of the word-major explicit mask (include/hta.h)."""
+    B, T = desc.batch, desc.tree_size
+    t_pad = T + (T & 1)
+    n = int(load().hta_dense_mask_bytes(ctypes.byref(desc)))
+    if n == 0:
+        _check(2, "hta_dense_mask_bytes")
+    return B, n // (8 * B * t_pad), t_pad
+
+
+def hta_dense_mask(desc, parent_idx, prefix_len, mask, workspace, stream=None) -> None:
+    _contig(parent_idx, prefix_len, mask, workspace)
+    _check(load().hta_dense_mask(ctypes.byref(desc), _ptr(parent_idx), _ptr(prefix_len),
+                                 _ptr(mask), _ptr(workspace), workspace.numel(),
+                                 _stream(stream)), "hta_dense_mask")
+
+
+def hta_verify_dense(desc, q, k_prefix, v_prefix, k_tree, v_tree, mask, prefix_len, out, lse,
+                     stream=None) -> None:
+    _contig(q, k_prefix, v_prefix, k_tree, v_tree, mask, prefix_len, out, lse)
+    _check(load().hta_verify_dense(ctypes.byref(desc), _ptr(q), _ptr(k_prefix), _ptr(v_prefix),
+                                   _ptr(k_tree), _ptr(v_tree), _ptr(mask), _ptr(prefix_len),
+                                   _ptr(out), _ptr(lse), _stream(stream)), "hta_verify_dense")
+
+
+def verify_dense(q, k_prefix, v_prefix, k_tree, v_tree, parent_idx, prefix_len, *, scale=None,
+                 mask: Optional[torch.Tensor] = None, stream=None):
+    """The single-pass masked baseline: builds the explicit mask (unless one is given) and
+    runs one masked attention pass over all L + T keys.  Returns (out, lse, mask)."""
+    desc = desc_for(q, k_prefix, scale)
+    B, T, Hq, D = q.shape
+    if mask is None:
+        mask = torch.empty(*dense_mask_shape(desc), dtype=torch.int64, device=q.device)
+        ws = torch.empty(256 * ((4 * B + 255) // 256), dtype=torch.uint8, device=q.device)
+        hta_dense_mask(desc, parent_idx, prefix_len, mask, ws, stream)
+    out = torch.empty(B, T, Hq, D, dtype=torch.float32, device=q.device)
+    lse = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    hta_verify_dense(desc, q, k_prefix, v_prefix, k_tree, v_tree, mask, prefix_len, out, lse,
+                     stream)
+    return out, lse, mask
 
 
 def chunk_mass(desc, prefix_len, lse, workspace, stream=None):

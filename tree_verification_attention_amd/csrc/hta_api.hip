@@ -262,6 +262,43 @@ hta_status hta_chunk_mass(const hta_desc* desc, const int32_t* prefix_len, const
                                            (hipStream_t)stream));
 }
 
+size_t hta_dense_mask_bytes(const hta_desc* desc) {
+  Geometry G;
+  if (make_plan(desc, &G, nullptr) != HTA_OK) return 0;
+  int32_t wp, wm, t_pad;
+  hta::dense_mask_words(G, &wp, &wm, &t_pad);
+  return sizeof(uint64_t) * (size_t)G.B * wm * t_pad;
+}
+
+hta_status hta_dense_mask(const hta_desc* desc, const int32_t* parent_idx,
+                          const int32_t* prefix_len, uint64_t* mask, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  Geometry G;
+  hta_plan_info p;
+  HTA_TRY(make_plan(desc, &G, &p));
+  HTA_TRY(check_ptrs({parent_idx, prefix_len, mask}));
+  if ((size_t)G.B > 65535) return HTA_ERR_SHAPE;
+  if (!workspace || workspace_bytes < p.masks_offset) return HTA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return HTA_ERR_ALIGN;
+  const Workspace ws = carve(workspace, p);
+  return hip_status(hta::launch_dense_mask(G, parent_idx, prefix_len, mask, ws.status,
+                                           (hipStream_t)stream));
+}
+
+hta_status hta_verify_dense(const hta_desc* desc, const void* q, const void* k_prefix,
+                            const void* v_prefix, const void* k_tree, const void* v_tree,
+                            const uint64_t* mask, const int32_t* prefix_len, float* out,
+                            float* lse, void* stream) {
+  Geometry G;
+  HTA_TRY(make_plan(desc, &G, nullptr));
+  if (G.f32) return HTA_ERR_DTYPE;
+  HTA_TRY(check_ptrs({q, k_tree, v_tree, mask, prefix_len, out, lse}));
+  if (G.Lmax > 0) HTA_TRY(check_ptrs({k_prefix, v_prefix}));
+  if ((size_t)G.B > 65535 || (size_t)G.Hkv > 65535) return HTA_ERR_SHAPE;
+  return hip_status(hta::launch_dense_masked(G, q, k_prefix, v_prefix, k_tree, v_tree, mask,
+                                             prefix_len, out, lse, (hipStream_t)stream));
+}
+
 }  // extern "C"
 
 namespace {

@@ -140,6 +140,18 @@ hipError_t launch_chunk_mass(const Geometry& g, const int32_t* prefix_len, const
                              float* mass, float* scores, const Workspace& ws,
                              hipStream_t stream);
 
+// The single-pass masked attention over all L + T keys (the method's "before"): explicit
+// mask uint64 [B, Wm, T_pad] (word-major) with Wp prefix words then ceil(T / 64) tree words
+// per node, T_pad = T rounded up to even.
+void dense_mask_words(const Geometry& g, int32_t* wp, int32_t* wm, int32_t* t_pad);
+hipError_t launch_dense_mask(const Geometry& g, const int32_t* parent_idx,
+                             const int32_t* prefix_len, uint64_t* mask, int32_t* status,
+                             hipStream_t stream);
+hipError_t launch_dense_masked(const Geometry& g, const void* q, const void* k_prefix,
+                               const void* v_prefix, const void* k_tree, const void* v_tree,
+                               const uint64_t* mask, const int32_t* prefix_len, float* out,
+                               float* lse, hipStream_t stream);
+
 // How the prefix pass blocks the query rows of one KV head: mt full row tiles per wave,
 // tiles_per_block row tiles per workgroup, blocks workgroups per (sequence, KV head, chunk).
 void prefix_row_blocking(const Geometry& g, int* mt, int* tiles_per_block, int* blocks);
