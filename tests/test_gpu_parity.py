@@ -392,3 +392,36 @@ def test_fp32_invalid_tree_and_prefix_len():
     out, lse = run_gpu(w)
     assert np.all(np.isnan(out[1])) and np.all(np.isnan(lse[1]))
     assert np.all(np.isfinite(out[0])) and np.all(np.isfinite(lse[0]))
+
+
+def test_stale_workspace_is_never_read():
+    """A workspace whose every byte is 0xFF (NaN in every float slot) before the call: the
+    whole step, the prefix-only merge (its tree slot is never written) and the drafter's
+    cross-attention must not pick up anything they did not write themselves."""
+    gen = torch.Generator().manual_seed(12)
+    par = [W.level_tree((2, 6), gen) for _ in range(3)]
+    w = W.make_workload("stale_ws", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                        max_prefix_len=900, parents=par, prefix_len=[900, 0, 333],
+                        poison_padding=True, seed=13)
+    t = to_dev(w)
+    desc = hta.desc_for(t["q"], t["k_prefix"], w.scale, 256)
+    B, T, Hq, D = w.q.shape
+    for mode in ("verify", "prefix_only", "cross"):
+        ws = torch.full((hta.workspace_size(desc),), 0xFF, dtype=torch.uint8, device="cuda")
+        out = torch.empty(B, T, Hq, D, dtype=torch.float32, device="cuda")
+        lse = torch.empty(B, Hq, T, dtype=torch.float32, device="cuda")
+        if mode == "verify":
+            hta.hta_verify(desc, t["q"], t["k_prefix"], t["v_prefix"], t["k_tree"], t["v_tree"],
+                           t["parent_idx"], t["prefix_len"], out, lse, ws)
+            part = oracle.PART_ALL
+        elif mode == "prefix_only":
+            hta.hta_prefix_partials(desc, t["q"], t["k_prefix"], t["v_prefix"], t["prefix_len"], ws)
+            hta.hta_merge(desc, t["prefix_len"], False, out, lse, ws)
+            part = oracle.PART_PREFIX
+        else:
+            hta.hta_cross_attention(desc, t["q"], t["k_prefix"], t["v_prefix"], t["prefix_len"],
+                                    out, lse, ws)
+            part = oracle.PART_PREFIX
+        torch.cuda.synchronize()
+        _log(f"  stale workspace, {mode}")
+        check_rows(w, out.cpu().double().numpy(), lse.cpu().double().numpy(), part=part)

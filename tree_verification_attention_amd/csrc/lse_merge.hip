@@ -329,13 +329,16 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   float acc[DPL];
   float wl = 0.f;  // this group's weight sum
   {
-    const float wt = (tree_slot && pg == 0) ? __builtin_amdgcn_exp2f((lse_tree - Mn) * kLog2e) : 0.f;
+    // the tree partial enters only when it is part of the merge: a select, not a weight of
+    // 0 (the slot is not written otherwise and may hold anything, NaN included)
+    const bool use_tree = tree_slot && pg == 0;
+    const float wt = use_tree ? __builtin_amdgcn_exp2f((lse_tree - Mn) * kLog2e) : 0.f;
     wl += wt;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const f32x4 t = unpack24(vt[j]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[4 * j + e] = wt * t[e];
+      for (int e = 0; e < 4; ++e) acc[4 * j + e] = use_tree ? wt * t[e] : 0.f;
     }
   }
   auto add_part = [&](float l, const Packed24 (&pv)[NV]) {
