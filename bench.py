@@ -318,6 +318,60 @@ def bench_around(w: W.Workload, dev, stream, steps: int, warmup: int) -> dict:
     }
 
 
+def bench_drafter(w: W.Workload, dev, stream, steps: int, kps, vps, n_copies: int) -> dict:
+    """The drafter's attention on the same target cache, HIP events on the launch stream:
+    cross-attention of one drafted level (16 queries) into the target's KV cache, and the
+    windowed self-attention (512-position ring as the prefix) of a 4,16 draft tree."""
+    B, T, Hq, D = w.q.shape
+    Hkv = w.num_kv_heads
+    gen = torch.Generator().manual_seed(w.seed + 11)
+    qc = torch.randn(B, 16, Hq, D, generator=gen).to(w.dtype).to(dev)
+    plen = w.prefix_len.to(dev)
+    dc = hta.desc_for(qc, kps[0], w.scale)
+    wsc = hta.new_workspace(dc, dev)
+    oc = torch.empty(B, 16, Hq, D, dtype=torch.float32, device=dev)
+    lc = torch.empty(B, Hq, 16, dtype=torch.float32, device=dev)
+    win = 512
+    par = torch.tensor([W.level_tree((4, 16), gen) for _ in range(B)], dtype=torch.int32,
+                       device=dev)
+    Tw = par.shape[1]
+    qw = torch.randn(B, Tw, Hq, D, generator=gen).to(w.dtype).to(dev)
+    kr = torch.randn(B, Hkv, win, D, generator=gen).to(w.dtype).to(dev)
+    vr = torch.randn(B, Hkv, win, D, generator=gen).to(w.dtype).to(dev)
+    kt = torch.randn(B, Hkv, Tw, D, generator=gen).to(w.dtype).to(dev)
+    vt = torch.randn(B, Hkv, Tw, D, generator=gen).to(w.dtype).to(dev)
+    wl = torch.full((B,), win, dtype=torch.int32, device=dev)
+    dw = hta.desc_for(qw, kr, w.scale)
+    wsw = hta.new_workspace(dw, dev)
+    ow = torch.empty(B, Tw, Hq, D, dtype=torch.float32, device=dev)
+    lw = torch.empty(B, Hq, Tw, dtype=torch.float32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for k in range(50):
+            fn(k)
+        e0.record(stream)
+        for k in range(steps):
+            fn(k)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3
+
+    cross_us = timed(lambda k: hta.hta_cross_attention(dc, qc, kps[k % n_copies],
+                                                       vps[k % n_copies], plen, oc, lc, wsc,
+                                                       stream))
+    window_us = timed(lambda k: hta.hta_verify(dw, qw, kr, vr, kt, vt, par, wl, ow, lw, wsw,
+                                               stream))
+    kv_bytes = int(w.prefix_len.sum()) * Hkv * D * 2 * w.k_prefix.element_size()
+    log(f"[bench] drafter: cross-attention (16 queries) {cross_us:.2f} us, window self-attention "
+        f"(512 + 4,16 tree) {window_us:.2f} us")
+    return {
+        "cross_attention_us": round(cross_us, 3), "cross_attention_queries": 16,
+        "cross_attention_GBps": round(kv_bytes / (cross_us * 1e-6) / 1e9, 1),
+        "window_self_attention_us": round(window_us, 3), "window": win, "window_tree_nodes": Tw,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -558,6 +612,7 @@ def main() -> int:
         "note": "one masked pass over all L+T keys per (64 query rows, KV head), explicit "
                 "mask; before_over_after = (mask build + pass) / the hybrid step (HIP events)",
     }
+    result["drafter"] = bench_drafter(w, dev, stream, args.steps, kps, vps, n_copies)
     result["around_attention"] = bench_around(w, dev, stream, args.steps, args.warmup)
     peaks = measured_peaks(dev)
     log(f"[bench] measured peaks: {peaks}")

@@ -196,6 +196,44 @@ hta_status hta_chunk_mass(const hta_desc *desc, const int32_t *prefix_len, const
                           size_t workspace_bytes, void *stream);
 
 /*
+ * ---- The drafter's attention (paper summary, Summary: a one-block drafter with
+ *      sliding-window self-attention, window 512, and cross-attention into the target
+ *      model's KV cache) ----
+ *
+ * Cross-attention: the drafter's queries attend to one layer of the target's KV cache with
+ * no mask: desc->tree_size = Tq query tokens per sequence, desc->max_prefix_len = the cache
+ * capacity; q [B, Tq, Hq, D], k_cache / v_cache [B, Hkv, Lmax, D] (the prefix layout),
+ * cache_len [B] (keys j < cache_len[b] are seen) -> out [B, Tq, Hq, D] float, lse [B, Hq, Tq].
+ * Two launches: the split-K prefix pass and the merge of its partials (no tree part).  A
+ * sequence with cache_len 0 gets out 0, lse -inf; a cache_len outside [0, Lmax] gives NaN
+ * (no status word is written).
+ */
+hta_status hta_cross_attention(const hta_desc *desc, const void *q, const void *k_cache,
+                               const void *v_cache, const int32_t *cache_len, float *out,
+                               float *lse, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/*
+ * The drafter's sliding-window self-attention while it drafts a tree is hta_verify with its
+ * window cache as the prefix: the cache is a ring of `window` slots holding the K/V of the
+ * last `window` committed positions (position p in slot p % window; keys carry their
+ * positions through the rotary encoding, and attention over a set of keys does not depend
+ * on their order), desc->max_prefix_len = window, prefix_len[b] = min(committed, window);
+ * the draft tree's own nodes are seen under the tree mask as in verification.
+ *
+ * hta_window_commit appends the accepted path's drafter K/V rows (node accepted[b, k] of
+ * k_tree / v_tree [B, Hkv, T, D], k < accept_len[b]) to the ring [B, Hkv, window, D] at slots
+ * (win_pos[b] + k) % window, and advances win_pos[b] by accept_len[b] (in place).  Only the
+ * last `window` rows of a longer path are written.  accept_len outside [0, T] or a negative
+ * win_pos is a device error (HTA_ERR_PREFIX_LEN in the status, nothing written).  Only the
+ * status words of the workspace are written (any buffer of 4 * batch bytes rounded up to 256).
+ */
+hta_status hta_window_commit(const hta_desc *desc, int32_t window, void *k_win, void *v_win,
+                             const void *k_tree, const void *v_tree, const int32_t *accepted,
+                             const int32_t *accept_len, int32_t *win_pos, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
  * ---- Verification without the hybrid split: the method's "before" ----
  *
  * The paper summary (Summary; Key points, "Hybrid Tree Attention") says a tree mask keeps

@@ -333,3 +333,23 @@ def kv_commit(k_prefix: np.ndarray, v_prefix: np.ndarray, k_tree: np.ndarray,
             vp[b, :, L + k, :] = v_tree[b, :, node, :]
         pl[b] = L + n
     return kp, vp, pl, full
+
+
+def window_commit(k_win: np.ndarray, v_win: np.ndarray, k_tree: np.ndarray, v_tree: np.ndarray,
+                  accepted: np.ndarray, accept_len: np.ndarray, win_pos: np.ndarray):
+    """Append each sequence's accepted path to its ring of the last W positions.
+
+    The ring [B, Hkv, W, D] holds position p in slot p % W.  Path row k (node accepted[b, k])
+    is position win_pos[b] + k; rows are written in path order, so of a path longer than W
+    only its last W rows remain.  Returns new arrays (k_win, v_win, win_pos)."""
+    kw, vw = k_win.copy(), v_win.copy()
+    pos = np.array(win_pos, dtype=np.int32, copy=True)
+    B, Hkv, Wn, D = kw.shape
+    for b in range(B):
+        for k in range(int(accept_len[b])):
+            node = int(accepted[b, k])
+            slot = (int(win_pos[b]) + k) % Wn
+            kw[b, :, slot, :] = k_tree[b, :, node, :]
+            vw[b, :, slot, :] = v_tree[b, :, node, :]
+        pos[b] = int(win_pos[b]) + int(accept_len[b])
+    return kw, vw, pos

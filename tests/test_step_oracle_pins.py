@@ -412,3 +412,29 @@ def test_each_step_mutant_fails_a_pin(name, tmp_path):
             except (AssertionError, oracle.OracleError):
                 failed.append(pin)
     assert failed, f"mutant {name} survived every pin"
+
+
+def test_window_commit_keeps_the_last_positions():
+    """Commit a stream of paths into a small ring; afterwards slot s must hold the latest
+    committed position p with p % W == s (a closed form of the ring), checked against the
+    full history written out position by position."""
+    rng = np.random.default_rng(13)
+    B, Hkv, W, D, T = 2, 2, 5, 3, 7
+    kw = np.zeros((B, Hkv, W, D), dtype=np.float32)
+    vw = np.zeros_like(kw)
+    pos = np.zeros((B,), dtype=np.int32)
+    history = [[], []]  # per sequence: (k row, v row) of every committed position
+    for step in range(9):
+        kt = rng.standard_normal((B, Hkv, T, D)).astype(np.float32)
+        vt = rng.standard_normal((B, Hkv, T, D)).astype(np.float32)
+        n = rng.integers(0, T + 1, size=B).astype(np.int32)
+        acc = np.full((B, T), -1, dtype=np.int32)
+        for b in range(B):
+            acc[b, :n[b]] = rng.permutation(T)[:n[b]]
+            history[b] += [(kt[b, :, acc[b, k]], vt[b, :, acc[b, k]]) for k in range(n[b])]
+        kw, vw, pos = oracle.window_commit(kw, vw, kt, vt, acc, n, pos)
+        for b in range(B):
+            assert pos[b] == len(history[b])
+            for p in range(max(0, pos[b] - W), pos[b]):
+                assert np.array_equal(kw[b, :, p % W], history[b][p][0])
+                assert np.array_equal(vw[b, :, p % W], history[b][p][1])

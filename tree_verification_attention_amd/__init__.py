@@ -12,11 +12,13 @@ from .binding import (  # noqa: F401
     accept_workspace_size,
     ancestor_masks,
     chunk_mass,
+    cross_attention,
     dense_mask_shape,
     desc_for,
     hta_accept_commit,
     hta_ancestor_masks,
     hta_chunk_mass,
+    hta_cross_attention,
     hta_dense_mask,
     hta_get_device_status,
     hta_merge,
@@ -25,6 +27,7 @@ from .binding import (  # noqa: F401
     hta_tree_partials,
     hta_verify,
     hta_verify_dense,
+    hta_window_commit,
     load,
     make_desc,
     new_workspace,
@@ -39,7 +42,8 @@ from .binding import (  # noqa: F401
 
 __all__ = [
     "HtaError", "accept_commit", "accept_workspace_size", "ancestor_masks", "chunk_mass",
-    "dense_mask_shape", "desc_for", "hta_accept_commit", "hta_ancestor_masks", "hta_chunk_mass",
+    "cross_attention", "dense_mask_shape", "desc_for", "hta_cross_attention",
+    "hta_window_commit", "hta_accept_commit", "hta_ancestor_masks", "hta_chunk_mass",
     "hta_dense_mask", "hta_verify_dense", "verify_dense", "hta_get_device_status", "hta_merge",
     "hta_prefix_partials", "hta_rope_tree", "hta_tree_partials", "hta_verify", "load",
     "make_desc", "new_workspace", "partial_views", "plan", "rope_tree", "status_str", "verify",

@@ -39,6 +39,8 @@ EXPORTED = (
     "hta_merge",
     "hta_get_device_status",
     "hta_chunk_mass",
+    "hta_cross_attention",
+    "hta_window_commit",
     "hta_dense_mask_bytes",
     "hta_dense_mask",
     "hta_verify_dense",
@@ -111,6 +113,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.hta_get_device_status.argtypes = [D, P, P, ctypes.POINTER(ctypes.c_int32)]
     L.hta_rope_tree.argtypes = [D, ctypes.c_double, I, P, P, P, P, P, P, S, P]
     L.hta_chunk_mass.argtypes = [D, P, P, P, P, P, S, P]
+    L.hta_cross_attention.argtypes = [D, P, P, P, P, P, P, P, S, P]
+    L.hta_window_commit.argtypes = [D, I, P, P, P, P, P, P, P, P, S, P]
     L.hta_dense_mask_bytes.argtypes = [D]
     L.hta_dense_mask_bytes.restype = S
     L.hta_dense_mask.argtypes = [D, P, P, P, P, S, P]
@@ -124,7 +128,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for f in (L.hta_plan, L.hta_verify, L.hta_ancestor_masks, L.hta_prefix_partials,
               L.hta_tree_partials, L.hta_merge, L.hta_get_device_status, L.hta_version,
               L.hta_rope_tree, L.hta_accept_commit, L.hta_chunk_mass, L.hta_dense_mask,
-              L.hta_verify_dense):
+              L.hta_verify_dense, L.hta_cross_attention, L.hta_window_commit):
         f.restype = ctypes.c_int
     _lib = L
     return L
@@ -251,6 +255,36 @@ def hta_chunk_mass(desc, prefix_len, lse, mass, chunk_scores, workspace, stream=
     _check(load().hta_chunk_mass(ctypes.byref(desc), _ptr(prefix_len), _ptr(lse), _ptr(mass),
                                  _ptr(chunk_scores), _ptr(workspace), workspace.numel(),
                                  _stream(stream)), "hta_chunk_mass")
+
+
+def hta_cross_attention(desc, q, k_cache, v_cache, cache_len, out, lse, workspace,
+                        stream=None) -> None:
+    _contig(q, k_cache, v_cache, cache_len, out, lse, workspace)
+    _check(load().hta_cross_attention(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(cache_len), _ptr(out), _ptr(lse), _ptr(workspace),
+                                      workspace.numel(), _stream(stream)), "hta_cross_attention")
+
+
+def cross_attention(q, k_cache, v_cache, cache_len, *, scale=None, chunk: int = 0,
+                    workspace: Optional[torch.Tensor] = None, stream=None):
+    """The drafter's cross-attention into a target KV cache (no mask): (out, lse)."""
+    desc = desc_for(q, k_cache, scale, chunk)
+    B, Tq, Hq, D = q.shape
+    out = torch.empty(B, Tq, Hq, D, dtype=torch.float32, device=q.device)
+    lse = torch.empty(B, Hq, Tq, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(desc, q.device)
+    hta_cross_attention(desc, q, k_cache, v_cache, cache_len, out, lse, workspace, stream)
+    return out, lse
+
+
+def hta_window_commit(desc, window: int, k_win, v_win, k_tree, v_tree, accepted, accept_len,
+                      win_pos, workspace, stream=None) -> None:
+    _contig(k_win, v_win, k_tree, v_tree, accepted, accept_len, win_pos, workspace)
+    _check(load().hta_window_commit(ctypes.byref(desc), int(window), _ptr(k_win), _ptr(v_win),
+                                    _ptr(k_tree), _ptr(v_tree), _ptr(accepted),
+                                    _ptr(accept_len), _ptr(win_pos), _ptr(workspace),
+                                    workspace.numel(), _stream(stream)), "hta_window_commit")
 
 
 def dense_mask_shape(desc: hta_desc) -> Tuple[int, int, int]:

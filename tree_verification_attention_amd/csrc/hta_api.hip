@@ -262,6 +262,41 @@ hta_status hta_chunk_mass(const hta_desc* desc, const int32_t* prefix_len, const
                                            (hipStream_t)stream));
 }
 
+hta_status hta_cross_attention(const hta_desc* desc, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* cache_len, float* out,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  Geometry G;
+  hta_plan_info p;
+  HTA_TRY(make_plan(desc, &G, &p));
+  HTA_TRY(check_ptrs({q, cache_len, out, lse}));
+  if (G.Lmax > 0) HTA_TRY(check_ptrs({k_cache, v_cache}));
+  HTA_TRY(check_ws(p, workspace, workspace_bytes));
+  const Workspace ws = carve(workspace, p);
+  hipStream_t s = (hipStream_t)stream;
+  // the prefix pass, then the merge of the prefix partials alone (no tree part); the merge
+  // reads no status word when the tree partial is left out
+  HTA_TRY(hip_status(launch_prefix(G, q, k_cache, v_cache, cache_len, ws, s)));
+  return hip_status(hta::launch_lse_merge(G, cache_len, false, out, lse, ws, s));
+}
+
+hta_status hta_window_commit(const hta_desc* desc, int32_t window, void* k_win, void* v_win,
+                             const void* k_tree, const void* v_tree, const int32_t* accepted,
+                             const int32_t* accept_len, int32_t* win_pos, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  Geometry G;
+  hta_plan_info p;
+  HTA_TRY(make_plan(desc, &G, &p));
+  if (window < 1) return HTA_ERR_SHAPE;
+  HTA_TRY(check_ptrs({k_win, v_win, k_tree, v_tree, accepted, accept_len, win_pos}));
+  if (!workspace || workspace_bytes < p.masks_offset) return HTA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return HTA_ERR_ALIGN;
+  const Workspace ws = carve(workspace, p);
+  return hip_status(hta::launch_window_commit(G, window, k_win, v_win, k_tree, v_tree, accepted,
+                                              accept_len, win_pos, ws.status,
+                                              (hipStream_t)stream));
+}
+
 size_t hta_dense_mask_bytes(const hta_desc* desc) {
   Geometry G;
   if (make_plan(desc, &G, nullptr) != HTA_OK) return 0;

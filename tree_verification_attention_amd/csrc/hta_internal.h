@@ -134,6 +134,12 @@ hipError_t launch_accept_commit(const Geometry& g, int32_t vocab, bool logits_f3
                                 int32_t* accept_len, int32_t* accepted, int32_t* bonus,
                                 int32_t* status, uint64_t* keys, hipStream_t stream);
 
+// The drafter's window ring: the accepted path's rows appended at slots (pos + k) % window.
+hipError_t launch_window_commit(const Geometry& g, int32_t window, void* k_win, void* v_win,
+                                const void* k_tree, const void* v_tree, const int32_t* accepted,
+                                const int32_t* accept_len, int32_t* win_pos, int32_t* status,
+                                hipStream_t stream);
+
 // Each chunk's (and the tree's) share of every query row's attention from the partial
 // log-sum-exps in the workspace and the rows' final log-sum-exps; optional per-sequence means.
 hipError_t launch_chunk_mass(const Geometry& g, const int32_t* prefix_len, const float* lse,

@@ -514,9 +514,89 @@ __global__ __launch_bounds__(kThreads) void accept_commit(AcceptArgs a) {
   if (tid == 0) a.prefix_len[b] = L + n;
 }
 
+// ----------------------------------------------------------------------------- drafter window
+
+struct WindowArgs {
+  void* k_win;  // [B, Hkv, W, D] ring: position p lives in slot p % W
+  void* v_win;
+  const void* k_tree;  // [B, Hkv, T, D]
+  const void* v_tree;
+  const int32_t* accepted;    // [B, T]
+  const int32_t* accept_len;  // [B]
+  int32_t* win_pos;           // [B] committed positions so far (in/out)
+  int32_t* status;
+  int32_t T, Hkv, W;
+  int32_t row_bytes;
+};
+
+// One workgroup per sequence: the accepted path's rows go to ring slots (pos + k) % W; when
+// the path is longer than the ring only its last W rows are written (no two lanes write one
+// slot); pos advances by the path length.
+__global__ __launch_bounds__(kThreads) void window_commit(WindowArgs a) {
+  constexpr int kBatch = 4;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int n = a.accept_len[b];
+  const int pos = a.win_pos[b];
+  const bool bad = n < 0 || n > a.T || pos < 0;
+  if (tid == 0) a.status[b] = bad ? kStatusPrefixLen : 0;
+  if (bad) return;
+  const int k0 = n > a.W ? n - a.W : 0;  // rows the ring keeps
+  const int rows = n - k0;
+  const int units = a.row_bytes / 16;
+  const int per_tensor = rows * a.Hkv * units;
+  for (int u0 = 0; u0 < 2 * per_tensor; u0 += kBatch * kThreads) {
+    uint4 val[kBatch];
+    uint4* dst[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int u = u0 + j * kThreads + tid;
+      dst[j] = nullptr;
+      if (u < 2 * per_tensor) {
+        const int is_v = u >= per_tensor;
+        const int v = u - is_v * per_tensor;
+        const int c = v % units, r = v / units;
+        const int k = k0 + r % rows, g = r / rows;
+        const int node = a.accepted[(size_t)b * a.T + k];
+        const int slot = (int)(((long long)pos + k) % a.W);
+        const char* src = (const char*)(is_v ? a.v_tree : a.k_tree) +
+                          (((size_t)b * a.Hkv + g) * a.T + node) * a.row_bytes;
+        dst[j] = (uint4*)((char*)(is_v ? a.v_win : a.k_win) +
+                          (((size_t)b * a.Hkv + g) * a.W + slot) * a.row_bytes) + c;
+        val[j] = ((const uint4*)src)[c];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (dst[j]) *dst[j] = val[j];
+  }
+  __syncthreads();  // every lane has read win_pos[b]
+  if (tid == 0) a.win_pos[b] = pos + n;
+}
+
 }  // namespace
 
 // ----------------------------------------------------------------------------- launchers
+
+hipError_t launch_window_commit(const Geometry& g, int32_t window, void* k_win, void* v_win,
+                                const void* k_tree, const void* v_tree, const int32_t* accepted,
+                                const int32_t* accept_len, int32_t* win_pos, int32_t* status,
+                                hipStream_t stream) {
+  WindowArgs a;
+  a.k_win = k_win;
+  a.v_win = v_win;
+  a.k_tree = k_tree;
+  a.v_tree = v_tree;
+  a.accepted = accepted;
+  a.accept_len = accept_len;
+  a.win_pos = win_pos;
+  a.status = status;
+  a.T = g.T;
+  a.Hkv = g.Hkv;
+  a.W = window;
+  a.row_bytes = g.D * (g.f32 ? 4 : 2);
+  hipLaunchKernelGGL(window_commit, dim3(g.B), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_rope_tree(const Geometry& g, double theta, bool interleaved, void* q,
                             void* k_tree, const int32_t* parent_idx, const int32_t* prefix_len,
