@@ -196,7 +196,7 @@ def test_verify_small_shapes(D, G):
 
 
 @pytest.mark.parametrize("G,T", [(4, 4), (8, 4), (4, 40), (2, 68), (4, 36), (4, 68), (1, 64),
-                                 (5, 50), (16, 17), (8, 40)])
+                                 (5, 50), (16, 17), (8, 40), (4, 12), (4, 16)])
 def test_verify_row_tilings(G, T):
     """Row counts T*G covering every way the prefix pass splits query-row tiles over its
     waves: 1 or 2 tiles only, leftover tiles of 1 and 2 (their keys split over waves),

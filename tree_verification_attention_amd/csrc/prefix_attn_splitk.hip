@@ -126,7 +126,17 @@ struct PrefixArgs {
 
 // MT full row tiles per wave (both wave groups); NL leftover tiles (0..2) per block, split
 // over the first wave group by keys.
-template <int D, int MT, int NL>
+// What one call of the pass lambdas does: leftover keys (value) and own row tiles (rows).
+template <bool WL, bool ROWS>
+struct PassTag {
+  static constexpr bool value = WL;
+  static constexpr bool rows = ROWS;
+};
+
+// BROWS: the second wave group owns row tiles.  With at most 4 row tiles per block the first
+// group holds them all and the second only builds V^T (no scores, softmax or PV of padding
+// rows on the SIMDs the first group's waves share).
+template <int D, int MT, int NL, bool BROWS>
 __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) {
   using Y = Layout<D>;
   constexpr int DS = D / 32;  // 32-wide d steps of the score product
@@ -294,6 +304,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   // keys 32 h + 16 j + 4 grp + r in sc[.][j][r]; keys past the chunk end get -inf
   auto scores = [&](auto tag, int t, int h, f32x4 (&sc)[MTA][2], f32x4 (&scl)[2]) {
     constexpr bool WL = decltype(tag)::value;
+    constexpr int MTE = decltype(tag)::rows ? MT : 0;  // row tiles this wave computes
     __builtin_amdgcn_sched_barrier(0);
     const unsigned char* Ks = lds + ring_slot(Y::kKRing, t, kKStages);
     const int key0 = kbeg + t * kKeyTile;
@@ -310,17 +321,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
 #pragma unroll
-        for (int k = 0; k < MT; ++k)
+        for (int k = 0; k < MTE; ++k)
           sc[k][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ds][j], qop[k][ds],
                                                              ds ? sc[k][j] : zero4, 0, 0, 0);
       }
     }
     // instruction order: operand reads run two d-steps ahead of the products
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+    if constexpr (MTE > 0) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * MT, 0);
-      if (ds + 2 < DS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      for (int ds = 0; ds < DS; ++ds) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * MTE, 0);
+        if (ds + 2 < DS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     // leftover scores of this wave's key blocks (the half's K operands are in registers):
@@ -350,7 +363,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
         for (int r = 0; r < 4; ++r)
           if (key0 + 32 * h + 16 * j + 4 * grp + r >= kend) {
 #pragma unroll
-            for (int k = 0; k < MT; ++k) sc[k][j][r] = -INFINITY;
+            for (int k = 0; k < MTE; ++k) sc[k][j][r] = -INFINITY;
           }
       if constexpr (WL) {
         if (h == lh) {
@@ -368,11 +381,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   // always holds a valid key)
   auto set_reference = [&](auto tag) {
     constexpr bool WL = decltype(tag)::value;
+    constexpr int MTE = decltype(tag)::rows ? MT : 0;
     f32x4 sc[MTA][2];
     f32x4 scl[2];
     scores(tag, 0, 0, sc, scl);
 #pragma unroll
-    for (int k = 0; k < MT; ++k) {
+    for (int k = 0; k < MTE; ++k) {
       const float m0 = fmaxf(fmaxf(sc[k][0][0], sc[k][0][1]), fmaxf(sc[k][0][2], sc[k][0][3]));
       const float m1 = fmaxf(fmaxf(sc[k][1][0], sc[k][1][1]), fmaxf(sc[k][1][2], sc[k][1][3]));
       m_ref[k] = group_max(fmaxf(m0, m1) * a.c);
@@ -393,6 +407,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   // ---- softmax of the scores of half h (from scores()): probabilities, P^T operands
   auto softmax = [&](auto tag, int h, f32x4 (&sc)[MTA][2], f32x4 (&scl)[2]) {
     constexpr bool WL = decltype(tag)::value;
+    constexpr int MTE = decltype(tag)::rows ? MT : 0;
     // ---- probabilities against the running reference (fp32)
     float p[MTA][8], pl[8], ls[MTA], lsl = 0.f;
     // (sums as a tree: short dependency chains)
@@ -400,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
       return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
     };
 #pragma unroll
-    for (int k = 0; k < MT; ++k) {
+    for (int k = 0; k < MTE; ++k) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         p[k][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[k][e / 4][e % 4], a.c, -m_ref[k]));
@@ -420,14 +435,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     // reference starts at the maximum of the chunk's first 32 keys); wave-uniform branch
     bool need = false;
 #pragma unroll
-    for (int k = 0; k < MT; ++k) need |= ls[k] > kRaiseP;
+    for (int k = 0; k < MTE; ++k) need |= ls[k] > kRaiseP;
     if constexpr (WL) need |= lhere && lsl > kRaiseP;
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
       // an empty volatile asm keeps this block a real (rarely taken) branch: without it the
       // compiler executes the rescale unconditionally, which doubles the VALU work per step
       asm volatile("" ::: "memory");
 #pragma unroll
-      for (int k = 0; k < MT; ++k) {
+      for (int k = 0; k < MTE; ++k) {
         const float mx = group_max(ls[k]);
         // mx bounds the row's largest probability from above: the new reference is at least
         // the row's largest score so far, so every probability drops to at most 1
@@ -458,7 +473,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     }
     // P^T operand of k-step h: element e <-> key 32 h + 16 (e / 4) + 4 grp + (e % 4)
 #pragma unroll
-    for (int k = 0; k < MT; ++k) {
+    for (int k = 0; k < MTE; ++k) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) pop[k][e] = (_Float16)p[k][e];
       l_run[k] += ls[k];
@@ -480,6 +495,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   // ---- PV(t, h): O^T[d][row] += V^T[d][key] P^T[key][row] for keys 32 h .. 32 h + 31 of tile t
   auto pv = [&](auto tag, int t, int h) {
     constexpr bool WL = decltype(tag)::value;
+    constexpr int MTE = decltype(tag)::rows ? MT : 0;
     __builtin_amdgcn_sched_barrier(0);
     const unsigned char* Vt = lds + ring_slot(Y::kVt, t, kVtStages) + vt_lane[h];
     f16x8 vop[DB];
@@ -488,14 +504,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int k = 0; k < MT; ++k)
+      for (int k = 0; k < MTE; ++k)
         acc[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[db], pop[k], acc[k][db], 0, 0, 0);
     // instruction order: operand reads run four d-blocks ahead of the products
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
+    if constexpr (MTE > 0) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, MT, 1);
-      if (db + 4 < DB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 1);
+      for (int db = 0; db < DB; ++db) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, MTE, 1);
+        if (db + 4 < DB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 1);
+      }
     }
     if constexpr (WL) {
       // leftover rows: this wave's key block(s) of the half, all D dims, from the same V^T
@@ -535,7 +553,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   // VALU phase.
   auto run_chunk = [&](auto group) {
     constexpr bool LAG = decltype(group)::value;  // second wave group
-    constexpr std::integral_constant<bool, !LAG && LEFT> tag{};
+    constexpr PassTag<!LAG && LEFT, !LAG || BROWS> tag{};
     // Prologue: tiles 0 and 1 (the first iteration needs both) and the query operands, then
     // tile 2.  The compiler does not count direct loads, so it would wait for every one of
     // them (vmcnt(0)) before the first use of the query registers; an explicit full wait
@@ -664,9 +682,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   }
 }
 
-template <int D, int MT, int NL>
+template <int D, int MT, int NL, bool BROWS = true>
 hipError_t launch_cfg(const PrefixArgs& a, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((prefix_attn_splitk<D, MT, NL>), grid, dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((prefix_attn_splitk<D, MT, NL, BROWS>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -680,8 +698,11 @@ hipError_t launch_mt(const PrefixArgs& a, int nl, dim3 grid, hipStream_t stream)
   }
 }
 
+// tiles_per_block <= 4 with one tile per wave: the first group holds every tile
 template <int D>
 hipError_t launch_d(const PrefixArgs& a, int mt, int nl, dim3 grid, hipStream_t stream) {
+  if (mt == 1 && nl == 0 && a.tiles_per_block <= kWaves / 2)
+    return launch_cfg<D, 1, 0, false>(a, grid, stream);
   switch (mt) {
     case 0: return launch_mt<D, 0>(a, nl, grid, stream);
     case 1: return launch_mt<D, 1>(a, nl, grid, stream);
