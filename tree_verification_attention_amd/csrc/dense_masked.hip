@@ -98,6 +98,18 @@ __device__ __forceinline__ void tr_read8(i16x4 (&r)[8], const uint32_t (&addr)[8
       : "memory");
 }
 
+__device__ __forceinline__ void tr_read4(i16x4 (&r)[4], const uint32_t (&addr)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3])
+      : "memory");
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void dense_masked(DenseArgs a) {
   constexpr int DS = D / 32, DB = D / 16;
@@ -106,7 +118,11 @@ __global__ __launch_bounds__(kThreads) void dense_masked(DenseArgs a) {
   // one LDS buffer: per stage the K tile, the V tile and each wave's mask words
   constexpr int kMaskBytes = kWaves * kMaskWords * 8;
   constexpr int kStageBytes = 2 * kTileBytes + kMaskBytes;
-  __shared__ __attribute__((aligned(1024))) unsigned char s_lds[kStages * kStageBytes];
+  // after the ring: one fp16 V^T tile in PV operand order, built by the four waves together
+  // (unit u = 2 db + h holds lane l's 16-byte operand at (u * 64 + l) * 16)
+  constexpr int kUnits = 2 * DB, kUnitsPerWave = kUnits / kWaves;
+  __shared__ __attribute__((aligned(1024))) unsigned char s_lds[kStages * kStageBytes + kTileBytes];
+  unsigned char* const s_vt = s_lds + kStages * kStageBytes;
   auto k_tile = [&](int st) { return s_lds + st * kStageBytes; };
   auto v_tile = [&](int st) { return s_lds + st * kStageBytes + kTileBytes; };
   auto mask_words = [&](int st, int w) {
@@ -204,6 +220,36 @@ __global__ __launch_bounds__(kThreads) void dense_masked(DenseArgs a) {
     else wait_and_barrier<0>();
   };
 
+  // this wave's quarter of V^T(t): tr reads of the V tile, widened bf16 -> fp16
+  auto build_vt = [&](int t) {
+    const unsigned char* Vs = v_tile(t % kStages);
+    const uint32_t vbase =  // the tile's LDS byte address
+        (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char*)Vs;
+    uint32_t addr[2 * kUnitsPerWave];
+#pragma unroll
+    for (int j = 0; j < kUnitsPerWave; ++j) {
+      const int u = wave * kUnitsPerWave + j, db = u >> 1, h = u & 1;
+      const int r0 = 32 * h + vrow, r1 = r0 + 16;
+      const int ch = 2 * db + vch;
+      addr[2 * j] = vbase + r0 * (2 * D) + 16 * (ch ^ swz_v<D>(r0)) + vhalf;
+      addr[2 * j + 1] = vbase + r1 * (2 * D) + 16 * (ch ^ swz_v<D>(r1)) + vhalf;
+    }
+    i16x4 rd[2 * kUnitsPerWave];
+    if constexpr (kUnitsPerWave == 4) tr_read8(rd, addr);
+    else tr_read4(rd, addr);
+#pragma unroll
+    for (int j = 0; j < kUnitsPerWave; ++j) {
+      f16x8 vop;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vop[e] = bf16_to_f16(rd[2 * j][e]);
+        vop[4 + e] = bf16_to_f16(rd[2 * j + 1][e]);
+      }
+      const int u = wave * kUnitsPerWave + j;
+      *(f16x8*)(s_vt + (u * 64 + lane) * 16) = vop;
+    }
+  };
+
   // Software-pipelined by one tile: the scores of tile t+1 enter the matrix core before the
   // softmax and PV product of tile t, so a wave's matrix work and its VALU and LDS work
   // overlap (one wave per SIMD: nothing else would hide them).
@@ -222,26 +268,33 @@ __global__ __launch_bounds__(kThreads) void dense_masked(DenseArgs a) {
     const int st = t % kStages;
     const bool tree = t >= ntp;
     const int kend = tree ? T - (t - ntp) * kKeyTile : Lc - t * kKeyTile;  // valid keys here
-    const unsigned char* Vs = v_tile(st);
-    const uint64_t mw = mask_words(st, wave)[mslot];
+    build_vt(t);
+    lds_done_barrier();  // V^T(t) complete (the last reads of the previous one are done)
+    // the node's visible keys of this tile (keys past the valid range cleared once), then
+    // the lane's four-key nibble of each 16-key block
+    uint64_t mw = mask_words(st, wave)[mslot];
+    if (kend < 64) mw &= (1ull << kend) - 1;
     float tmax = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint32_t nib = (uint32_t)(mw >> (16 * kb + 4 * grp)) & 0xFu;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int k = kb * 16 + 4 * grp + i;
-        const bool vis = k < kend && ((mw >> k) & 1ull);
-        const float x = vis ? sc[kb][i] * c : -INFINITY;
+        const float x = (nib >> i) & 1u ? sc[kb][i] * c : -INFINITY;
         sc[kb][i] = x;
         tmax = fmaxf(tmax, x);
       }
+    }
     const float m_new = fmaxf(m_run, group_max(tmax));
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    l_run *= alpha;
+    // rescale only when some row's maximum rose (after the first tiles, rarely)
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    }
+    m_run = m_new;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       f16x8 pop;
@@ -251,31 +304,12 @@ __global__ __launch_bounds__(kThreads) void dense_masked(DenseArgs a) {
         l_run += p;
         pop[e] = (_Float16)p;
       }
-      const int r0 = 32 * h + vrow, r1 = r0 + 16;
-      const uint32_t vbase =  // the tile's LDS byte address
-          (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char*)Vs;
+      f16x8 vop[DB];
 #pragma unroll
-      for (int d0 = 0; d0 < DB; d0 += 4) {  // four d blocks (eight reads) per wait
-        uint32_t addr[8];
-        i16x4 rd[8];
+      for (int db = 0; db < DB; ++db) vop[db] = *(const f16x8*)(s_vt + ((2 * db + h) * 64 + lane) * 16);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int ch = 2 * (d0 + j) + vch;
-          addr[2 * j] = vbase + r0 * (2 * D) + 16 * (ch ^ swz_v<D>(r0)) + vhalf;
-          addr[2 * j + 1] = vbase + r1 * (2 * D) + 16 * (ch ^ swz_v<D>(r1)) + vhalf;
-        }
-        tr_read8(rd, addr);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f16x8 vop;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            vop[e] = bf16_to_f16(rd[2 * j][e]);
-            vop[4 + e] = bf16_to_f16(rd[2 * j + 1][e]);
-          }
-          acc[d0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop, acc[d0 + j], 0, 0, 0);
-        }
-      }
+      for (int db = 0; db < DB; ++db)
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[db], pop, acc[db], 0, 0, 0);
     }
     lds_done_barrier();  // every wave is done with K(t+1) and V(t) before stages are refilled
 #pragma unroll
