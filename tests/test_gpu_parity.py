@@ -230,6 +230,34 @@ def test_verify_chunk_sizes_all_within_tolerance(chunk):
     check_rows(w, out, lse, n_rows=2000)
 
 
+def test_verify_more_than_64_splits():
+    """79 splits of 64 keys: the merge's pass over splits beyond its first 36 and its maximum
+    over splits beyond the first 64 (every row checked)."""
+    gen = torch.Generator().manual_seed(9)
+    par = [W.level_tree((2, 3, 3), gen), W.chain_tree(8)]
+    w = _small("splits79", par, B=2, Hq=8, Hkv=2, L=5000, plen=[5000, 4200], seed=9)
+    _log("verify 79 splits")
+    out, lse = run_gpu(w, chunk=64)
+    check_rows(w, out, lse)
+
+
+def test_million_token_prefix_sampled_rows():
+    """The longest prefix in the suite: the Llama-3-8B layer shape at 2^20 prefix tokens (4 GiB
+    of bf16 K/V, 128 splits of 8192 keys in the automatic plan)."""
+    w = W.llama3_8b(1 << 20, seed=1005)
+    t = to_dev(w)
+    desc = hta.desc_for(t["q"], t["k_prefix"], w.scale)
+    assert hta.plan(desc).num_splits == 128
+    _log(f"config {w.name}")
+    out, lse = hta.verify(t["q"], t["k_prefix"], t["v_prefix"], t["k_tree"], t["v_tree"],
+                          t["parent_idx"], t["prefix_len"], scale=w.scale)
+    torch.cuda.synchronize()
+    del t
+    out, lse = out.cpu().double().numpy(), lse.cpu().double().numpy()
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    check_rows(w, out, lse, n_rows=16, seed=3)
+
+
 @pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 8, 8), (128, 20, 4)])
 def test_late_score_spikes(D, Hq, Hkv):
     """Keys far above every score of their chunk's first 32 keys (the prefix pass must not
