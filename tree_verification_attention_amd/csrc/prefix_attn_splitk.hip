@@ -36,13 +36,14 @@
 //    store per lane) laid out in the exact key order of the P^T operand, so the PV product
 //    reads plain conflict-free 16-byte operands.  This runs one tile ahead of the compute.
 //  * Softmax in fp32 with exp2 (scale*log2(e) folded into one FMA) against a per-row
-//    reference: the maximum of the chunk's first 32 keys, raised only when a lane's
-//    probabilities of a 32-key half sum above 2^15 (a wave-wide ballot), so the accumulator
+//    reference: the maximum of the chunk's first 32 keys, raised only when a probability
+//    of a 32-key half would exceed 2^15 (a wave-wide ballot), so the accumulator
 //    rescale leaves the common path; the result is exact either way, since numerator and
 //    normaliser share the reference.  Probabilities enter the PV product as fp16
 //    (nearest-even, 11 significant bits, at most 2^15), V is widened from bf16 to fp16
-//    (exact for |v| in [2^-14, 65504]), and the normaliser sums the unrounded fp32
-//    probabilities.
+//    (exact for |v| in [2^-14, 65504]), and the normaliser adds those same rounded
+//    probabilities in fp32 (v_dot2 against (1, 1), two per instruction): numerator and
+//    normaliser weight every key alike, so a key that dominates its row comes out exact.
 #include "hta_internal.h"
 #include "lds_tiles.h"
 
@@ -60,7 +61,7 @@ constexpr int kVtStages = 3;  // V^T: tiles t-1 (PV of its last half), t, t+1 (b
 // instruction classes of the scheduling hints (__builtin_amdgcn_sched_group_barrier masks)
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
-constexpr float kRaiseP = 32768.f;  // probabilities stay below 2^15 (fp16 max 65504)
+constexpr float kRaiseLog2 = 15.f;  // probabilities stay at most 2^15 (fp16 max 65504)
 
 template <int D>
 struct Layout {
@@ -83,6 +84,20 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast
 
 __device__ __forceinline__ i16x4 tr_read_b64(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+
+// c + the fp16 values of v, added in fp32 two per instruction (v_dot2 against (1, 1))
+__device__ __forceinline__ float add_f16(f16x8 v, float c) {
+  const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+  c = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 0, 1), one, c, false);
+  c = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 2, 3), one, c, false);
+  c = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 4, 5), one, c, false);
+  return __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 6, 7), one, c, false);
+}
+__device__ __forceinline__ float add_f16(f16x4 v, float c) {
+  const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+  c = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 0, 1), one, c, false);
+  return __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 2, 3), one, c, false);
 }
 
 __device__ __forceinline__ _Float16 bf16_bits_to_f16(short h) {
@@ -295,9 +310,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   f16x8 popl;   // leftover P^T: NL = 2 (32 keys)
   f16x4 popl4;  // leftover P^T: NL = 1 (16 keys)
   // Softmax reference per row (log2 units): starts at the maximum of the chunk's first 32
-  // keys and is only raised when a lane's 8 probabilities of a half sum above kRaiseP, so
-  // p = 2^(s c - m_ref) <= 2^15 always fits fp16 and the accumulator rescale is rare (a
-  // lower bound raises the reference, and rescales, several times per chunk on peaky keys).
+  // keys and is only raised when a probability of a half would exceed 2^15 (an exponent
+  // above kRaiseLog2), so p = 2^(s c - m_ref) <= 2^15 always fits fp16 and the accumulator
+  // rescale is rare (a lower bound raises the reference, and rescales, several times per
+  // chunk on peaky keys).
   float m_ref[MTA], m_refl = 0.f;
 
   // ---- scores S^T[key][row] of keys 32 h .. 32 h + 31 of tile t: this lane holds row l16,
@@ -408,87 +424,97 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   auto softmax = [&](auto tag, int h, f32x4 (&sc)[MTA][2], f32x4 (&scl)[2]) {
     constexpr bool WL = decltype(tag)::value;
     constexpr int MTE = decltype(tag)::rows ? MT : 0;
-    // ---- probabilities against the running reference (fp32)
-    float p[MTA][8], pl[8], ls[MTA], lsl = 0.f;
-    // (sums as a tree: short dependency chains)
-    auto sum8 = [](const float (&v)[8]) {
-      return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    // ---- probabilities against the running reference (fp32), rounded to the fp16 P^T
+    // operands; the row sums add exactly those rounded values (in fp32), so numerator and
+    // normaliser weight every key alike.  ln: the running sum with this half's values.
+    float p[MTA][8], pl[8], ln[MTA], lnl = 0.f, xm[MTA], xml = -INFINITY;
+    auto make_ops = [&](int k) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pop[k][e] = (_Float16)p[k][e];
+      ln[k] = add_f16(pop[k], l_run[k]);
+    };
+    auto make_left = [&]() {
+      if constexpr (LKB == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) popl[e] = (_Float16)pl[e];
+        lnl = add_f16(popl, l_l);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) popl4[e] = (_Float16)pl[e];
+        lnl = add_f16(popl4, l_l);
+      }
+    };
+    // (the exponents' maximum decides the rare reference raise, off the path of the sums)
+    auto max8 = [](const float (&v)[8]) {
+      return fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
+                   fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
     };
 #pragma unroll
     for (int k = 0; k < MTE; ++k) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        p[k][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[k][e / 4][e % 4], a.c, -m_ref[k]));
-      ls[k] = sum8(p[k]);
+      for (int e = 0; e < 8; ++e) p[k][e] = __builtin_fmaf(sc[k][e / 4][e % 4], a.c, -m_ref[k]);
+      xm[k] = max8(p[k]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[k][e] = __builtin_amdgcn_exp2f(p[k][e]);
+      make_ops(k);
     }
     const bool lhere = WL && h == lh;  // this step carries the wave's leftover keys
     if constexpr (WL) {
       if (lhere) {
 #pragma unroll
-        for (int e = 0; e < 4 * LKB; ++e)
-          pl[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(scl[e / 4][e % 4], a.c, -m_refl));
-        if constexpr (LKB == 2) lsl = sum8(pl);
-        else lsl = (pl[0] + pl[1]) + (pl[2] + pl[3]);
+        for (int e = 0; e < 4 * LKB; ++e) pl[e] = __builtin_fmaf(scl[e / 4][e % 4], a.c, -m_refl);
+        if constexpr (LKB == 2) xml = max8(pl);
+        else xml = fmaxf(fmaxf(pl[0], pl[1]), fmaxf(pl[2], pl[3]));
+#pragma unroll
+        for (int e = 0; e < 4 * LKB; ++e) pl[e] = __builtin_amdgcn_exp2f(pl[e]);
+        make_left();
       }
     }
-    // ---- raise the reference of rows whose probabilities outgrew kRaiseP (rare: the
+    // ---- raise the reference of rows with a probability above 2^15 (rare: the
     // reference starts at the maximum of the chunk's first 32 keys); wave-uniform branch
     bool need = false;
 #pragma unroll
-    for (int k = 0; k < MTE; ++k) need |= ls[k] > kRaiseP;
-    if constexpr (WL) need |= lhere && lsl > kRaiseP;
+    for (int k = 0; k < MTE; ++k) need |= xm[k] > kRaiseLog2;
+    if constexpr (WL) need |= lhere && xml > kRaiseLog2;
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
       // an empty volatile asm keeps this block a real (rarely taken) branch: without it the
       // compiler executes the rescale unconditionally, which doubles the VALU work per step
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int k = 0; k < MTE; ++k) {
-        const float mx = group_max(ls[k]);
-        // mx bounds the row's largest probability from above: the new reference is at least
-        // the row's largest score so far, so every probability drops to at most 1
-        const float shift = mx > kRaiseP ? __log2f(mx) : 0.f;
+        // the row's largest exponent of the half: the new reference is at least the row's
+        // largest score so far, so every probability drops to at most 1
+        const float mx = group_max(xm[k]);
+        const float shift = mx > kRaiseLog2 ? mx : 0.f;
         const float alpha = __builtin_amdgcn_exp2f(-shift);
         m_ref[k] += shift;
         l_run[k] *= alpha;
-        ls[k] *= alpha;
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[k][e] *= alpha;
+        make_ops(k);
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[k][db] *= alpha;
       }
       if constexpr (WL) {
         if (lhere) {
-          const float mx = group_max(lsl);
-          const float shift = mx > kRaiseP ? __log2f(mx) : 0.f;
+          const float mx = group_max(xml);
+          const float shift = mx > kRaiseLog2 ? mx : 0.f;
           const float alpha = __builtin_amdgcn_exp2f(-shift);
           m_refl += shift;
           l_l *= alpha;
-          lsl *= alpha;
 #pragma unroll
           for (int e = 0; e < 4 * LKB; ++e) pl[e] *= alpha;
+          make_left();
 #pragma unroll
           for (int j = 0; j < DB; ++j) accl[j] *= alpha;
         }
       }
     }
-    // P^T operand of k-step h: element e <-> key 32 h + 16 (e / 4) + 4 grp + (e % 4)
+    // (P^T operand of k-step h: element e <-> key 32 h + 16 (e / 4) + 4 grp + (e % 4))
 #pragma unroll
-    for (int k = 0; k < MTE; ++k) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pop[k][e] = (_Float16)p[k][e];
-      l_run[k] += ls[k];
-    }
+    for (int k = 0; k < MTE; ++k) l_run[k] = ln[k];
     if constexpr (WL) {
-      if (lhere) {
-        if constexpr (LKB == 2) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) popl[e] = (_Float16)pl[e];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) popl4[e] = (_Float16)pl[e];
-        }
-        l_l += lsl;
-      }
+      if (lhere) l_l = lnl;
     }
   };
 
