@@ -47,8 +47,10 @@
  * Limits: head_dim in {64, 128}; 1 <= tree_size <= 256; num_q_heads % num_kv_heads == 0;
  * num_q_heads / num_kv_heads <= 16; every tensor pointer 16-byte aligned, the workspace
  * 256-byte aligned.  in_dtype HTA_BF16 runs the matrix-core kernels (bf16 products, fp32
- * accumulation, probabilities entering the PV product as fp16); HTA_F32 runs exact fp32
- * vector-ALU kernels meant for small validation shapes (same plan, workspace and layouts).
+ * accumulation, probabilities entering the PV product as fp16 and normalised by the sum of
+ * those same rounded values, so a prefix part's log-sum-exp is within 2^-11 of the exact
+ * one); HTA_F32 runs exact fp32 vector-ALU kernels meant for small validation shapes (same
+ * plan, workspace and layouts).
  */
 #ifndef HTA_H
 #define HTA_H
