@@ -241,6 +241,20 @@ def test_verify_more_than_64_splits():
     check_rows(w, out, lse)
 
 
+def test_largest_tree_and_group_at_32k():
+    """The largest tree (T = 256) with the largest query group (G = 16: 4096 query rows per KV
+    head, 16 row blocks of the prefix pass) over a 32k prefix, one random forest and one
+    LongSpec-style level tree."""
+    gen = torch.Generator().manual_seed(31)
+    par = [W.random_forest(256, gen), W.level_tree((4, 16, 16, 60, 80, 80), gen)]
+    w = _small("T256_G16_32k", par, B=2, Hq=32, Hkv=2, D=128, L=32768, plen=[32768, 20000],
+               seed=31)
+    _log("verify T=256 G=16 at 32k")
+    out, lse = run_gpu(w)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    check_rows(w, out, lse, n_rows=48, seed=4)
+
+
 def test_million_token_prefix_sampled_rows():
     """The longest prefix in the suite: the Llama-3-8B layer shape at 2^20 prefix tokens (4 GiB
     of bf16 K/V, 128 splits of 8192 keys in the automatic plan)."""
