@@ -329,6 +329,25 @@ def test_bitwise_deterministic():
 # ----------------------------------------------------------------------------- device errors
 
 
+def test_side_stream_matches_the_current_stream():
+    """The wrappers on a second torch stream (default priority): the same bits as on the
+    current stream, the outputs recorded on that stream by the wrapper."""
+    gen = torch.Generator().manual_seed(41)
+    par = [W.level_tree(W.LONGSPEC_TREE_WIDTHS, gen) for _ in range(2)]
+    w = _small("side_stream", par, B=2, Hq=8, Hkv=2, L=2000, plen=[2000, 1200], seed=41)
+    t = to_dev(w)
+    args = (t["q"], t["k_prefix"], t["v_prefix"], t["k_tree"], t["v_tree"], t["parent_idx"],
+            t["prefix_len"])
+    ref_out, ref_lse = hta.verify(*args, scale=w.scale)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        out, lse = hta.verify(*args, scale=w.scale, stream=side)
+    side.synchronize()
+    assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+
+
 def test_invalid_tree_is_flagged_and_poisons_only_its_sequence():
     gen = torch.Generator().manual_seed(12)
     good = W.level_tree((2, 3), gen)

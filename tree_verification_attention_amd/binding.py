@@ -170,6 +170,16 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _used_on(stream, *tensors) -> None:
+    """Tensors a wrapper allocated (on the current stream) and handed to work on another torch
+    stream: recorded on that stream, so the caching allocator does not reuse their memory
+    before the work there has finished.  (With a raw stream handle the caller passes its own
+    workspace and keeps the outputs alive until that stream has finished.)"""
+    if isinstance(stream, torch.cuda.Stream) and stream != torch.cuda.current_stream(stream.device):
+        for t in tensors:
+            t.record_stream(stream)
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return HTA_BF16
@@ -275,6 +285,7 @@ def cross_attention(q, k_cache, v_cache, cache_len, *, scale=None, chunk: int = 
     if workspace is None:
         workspace = new_workspace(desc, q.device)
     hta_cross_attention(desc, q, k_cache, v_cache, cache_len, out, lse, workspace, stream)
+    _used_on(stream, out, lse, workspace)
     return out, lse
 
 
@@ -322,10 +333,12 @@ def verify_dense(q, k_prefix, v_prefix, k_tree, v_tree, parent_idx, prefix_len, 
         mask = torch.empty(*dense_mask_shape(desc), dtype=torch.int64, device=q.device)
         ws = torch.empty(256 * ((4 * B + 255) // 256), dtype=torch.uint8, device=q.device)
         hta_dense_mask(desc, parent_idx, prefix_len, mask, ws, stream)
+        _used_on(stream, mask, ws)
     out = torch.empty(B, T, Hq, D, dtype=torch.float32, device=q.device)
     lse = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
     hta_verify_dense(desc, q, k_prefix, v_prefix, k_tree, v_tree, mask, prefix_len, out, lse,
                      stream)
+    _used_on(stream, out, lse)
     return out, lse, mask
 
 
@@ -337,6 +350,7 @@ def chunk_mass(desc, prefix_len, lse, workspace, stream=None):
     mass = torch.empty(B, Hq, T, p.num_splits + 1, dtype=torch.float32, device=lse.device)
     scores = torch.empty(B, p.num_splits + 1, dtype=torch.float32, device=lse.device)
     hta_chunk_mass(desc, prefix_len, lse, mass, scores, workspace, stream)
+    _used_on(stream, mass, scores)
     return mass, scores
 
 
@@ -386,6 +400,7 @@ def verify(q, k_prefix, v_prefix, k_tree, v_tree, parent_idx, prefix_len, *, sca
         workspace = new_workspace(desc, q.device)
     hta_verify(desc, q, k_prefix, v_prefix, k_tree, v_tree, parent_idx, prefix_len, out, lse,
                workspace, stream)
+    _used_on(stream, out, lse, workspace)
     return out, lse
 
 
@@ -399,6 +414,7 @@ def ancestor_masks(parent_idx: torch.Tensor, workspace: Optional[torch.Tensor] =
     if workspace is None:
         workspace = new_workspace(desc, parent_idx.device)
     hta_ancestor_masks(desc, parent_idx, masks, workspace, stream)
+    _used_on(stream, masks, workspace)
     return masks
 
 
@@ -419,6 +435,7 @@ def rope_tree(q, k_tree, parent_idx, prefix_len, rope_theta: float, *, interleav
         workspace = new_workspace(ws_desc, q.device)
     hta_rope_tree(desc, rope_theta, interleaved, q, k_tree, parent_idx, prefix_len, positions,
                   workspace, stream)
+    _used_on(stream, positions, workspace)
     return positions
 
 
@@ -443,6 +460,7 @@ def accept_commit(logits, tokens, root_token, parent_idx, prefix_len, k_prefix, 
     hta_accept_commit(desc, logits, tokens, root_token, parent_idx, prefix_len, k_prefix,
                       v_prefix, k_tree, v_tree, target_next, accept_len, accepted, bonus,
                       workspace, stream)
+    _used_on(stream, target_next, accept_len, accepted, bonus, workspace)
     return target_next, accept_len, accepted, bonus
 
 
