@@ -445,9 +445,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
       }
     };
     // (the exponents' maximum decides the rare reference raise, off the path of the sums)
-    auto max8 = [](const float (&v)[8]) {
-      return fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
-                   fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+    auto max8 = [](const float (&v)[8]) {  // four v_max3/v_max instructions
+      const float a = fmaxf(fmaxf(v[0], v[1]), v[2]);
+      const float b = fmaxf(fmaxf(v[3], v[4]), v[5]);
+      return fmaxf(b, fmaxf(fmaxf(v[6], v[7]), a));
     };
 #pragma unroll
     for (int k = 0; k < MTE; ++k) {
