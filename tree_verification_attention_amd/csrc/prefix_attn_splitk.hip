@@ -126,6 +126,21 @@ __device__ __forceinline__ void wait_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// The split-K partials leave through agent-scope stores (sc1): the merge reads them in the
+// next launch, possibly on other XCDs, whose L2s are not coherent with this one, so the
+// stores write through this XCD's L2 instead of waiting in it for the end-of-launch
+// write-back.  Raw buffer stores on a per-workgroup resource (dword 3 below: untyped dword
+// access on CDNA3/CDNA4); bytes past num_records are dropped, never written.
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kAgentScope = 16;  // the sc1 cache-policy bit
+typedef __attribute__((ext_vector_type(3))) unsigned u32x3;
+__device__ __forceinline__ void store24_agent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
+                                              f32x4 v) {
+  const Packed24 p = pack24(v);
+  __builtin_amdgcn_raw_buffer_store_b96(u32x3{p.w[0], p.w[1], p.w[2]}, r, byte_off, 0,
+                                        kAgentScope);
+}
+
 struct PrefixArgs {
   const unsigned short* q;         // bf16 bits [B, T, Hq, D]
   const unsigned short* k_prefix;  // [B, Hkv, Lmax, D]
@@ -625,6 +640,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
 
   // ---- normalise and write this chunk's partial
   const size_t slot = ((size_t)b * G.Hkv + kv) * (G.S + 1) + s;
+  const __amdgpu_buffer_rsrc_t part_rows = __builtin_amdgcn_make_buffer_rsrc(
+      a.o_part + slot * G.R_pad * (3 * D / 4), 0, G.R_pad * 3 * D, kBufWord3);
   // A lane holds 4 consecutive dims of one row per d block, so direct stores would write
   // small pieces of 16 rows per instruction.  Each wave stages its normalised rows in LDS
   // (the V and V^T rings are free once every wave is past its loop) and writes them back
@@ -652,7 +669,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
       for (int j = 0; j < 16 / kRowsPerInst; ++j) {
         const int rr = j * kRowsPerInst + lane / kC, c = lane % kC;
         const f32x4 v = *(const f32x4*)(stage + rr * D * 4 + 16 * (c ^ (rr & (kC - 1))));
-        store24(a.o_part + (slot * G.R_pad + tile * 16 + rr) * (3 * D / 4), c, v);
+        store24_agent(part_rows, ((tile * 16 + rr) * (3 * D / 4) + 3 * c) * 4, v);
       }
       if (grp == 0) a.lse_part[slot * G.R_pad + tile * 16 + l16] = (m_ref[k] + __log2f(lt)) * kLn2;
     }
@@ -695,14 +712,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
       }
       const float inv = 1.f / den;
       const int row = ltile * 16 + l16;
-      uint32_t* orow = a.o_part + (slot * G.R_pad + row) * (3 * D / 4);
 #pragma unroll
       for (int j = 0; j < kOwn; ++j) {
         f32x4 o = zero4;
 #pragma unroll
         for (int i = 0; i < kShare; ++i)
           o += wgt[i] * *(const f32x4*)(xl + ((w0 + i) * 64 + lane) * kStride + 4 * (o0 + j));
-        store24(orow, 4 * (o0 + j) + grp, o * inv);
+        store24_agent(part_rows, (row * (3 * D / 4) + 3 * (4 * (o0 + j) + grp)) * 4, o * inv);
       }
       if (grp == 0 && o0 == 0) a.lse_part[slot * G.R_pad + row] = (M + __log2f(den)) * kLn2;
     }
