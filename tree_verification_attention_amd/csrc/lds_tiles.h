@@ -26,11 +26,16 @@ __device__ __forceinline__ int swz_v(int row) {
   return D == 128 ? 2 * (row & 7) : 2 * (row & 3);
 }
 
+// Cache-policy bits of a direct load: kLoadStream marks data read once (non-temporal).
+constexpr int kLoadDefault = 0;
+constexpr int kLoadStream = 2;
+
 // One 16-byte-per-lane direct load from global memory into LDS.  The builtin only exists for
 // the device; the host pass parses this body without generating it.
+template <int POLICY = kLoadDefault>
 __device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, POLICY);
 #endif
 }
 
@@ -49,8 +54,8 @@ __device__ __forceinline__ const unsigned char* opaque_uniform(const void* p) {
 // re-read row kend-1 (callers mask those keys).  Each wave issues 64 * D * 2 / (1024 * nwaves)
 // loads per tensor.
 // With SKIP_PAST_END, 1 KB blocks that lie wholly at or past `kend` are not loaded at all
-// (their LDS contents stay undefined).
-template <int D, int NWAVES, bool SKIP_PAST_END = false>
+// (their LDS contents stay undefined).  POLICY: the loads' cache-policy bits.
+template <int D, int NWAVES, bool SKIP_PAST_END = false, int POLICY = kLoadDefault>
 __device__ __forceinline__ void dma_kv_tile(const unsigned short* Kg, const unsigned short* Vg,
                                             int key0, int kend, unsigned char* ks,
                                             unsigned char* vs, int w, int lane) {
@@ -72,8 +77,8 @@ __device__ __forceinline__ void dma_kv_tile(const unsigned short* Kg, const unsi
     for (int j = 0; j < kPerWave; ++j) {
       const size_t row0 = (size_t)key0 + j * NWAVES * kBlkRows;
       const int blk = j * NWAVES + w;
-      lds_dma16(opaque_uniform(Kg + row0 * D) + ko, ks + 1024 * blk);
-      lds_dma16(opaque_uniform(Vg + row0 * D) + vo, vs + 1024 * blk);
+      lds_dma16<POLICY>(opaque_uniform(Kg + row0 * D) + ko, ks + 1024 * blk);
+      lds_dma16<POLICY>(opaque_uniform(Vg + row0 * D) + vo, vs + 1024 * blk);
     }
     return;
   }
@@ -85,8 +90,8 @@ __device__ __forceinline__ void dma_kv_tile(const unsigned short* Kg, const unsi
     const int blk = j * NWAVES + w;  // 1 KB block of the tile written by this wave
     if (SKIP_PAST_END && blk * kBlkRows > last) continue;
     const uint32_t rr = (uint32_t)min(r0 + j * NWAVES * kBlkRows, last);
-    lds_dma16(kb + (2u * D * rr + kx), ks + 1024 * blk);
-    lds_dma16(vb + (2u * D * rr + vx), vs + 1024 * blk);
+    lds_dma16<POLICY>(kb + (2u * D * rr + kx), ks + 1024 * blk);
+    lds_dma16<POLICY>(vb + (2u * D * rr + vx), vs + 1024 * blk);
   }
 }
 

@@ -232,7 +232,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
 
   // ---- stream K/V tiles into the LDS rings
   auto issue = [&](int t) {
-    dma_kv_tile<D, 4>(Kg, Vg, kbeg + t * kKeyTile, kend,
+    // (each K/V byte is read once per pass: non-temporal loads)
+    dma_kv_tile<D, 4, false, kLoadStream>(Kg, Vg, kbeg + t * kKeyTile, kend,
                       lds + Y::kKRing + (t % kKStages) * Y::kTileBytes,
                       lds + Y::kVRing + (t % kVStages) * Y::kTileBytes, ww, lane);
   };
