@@ -178,10 +178,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   __shared__ __attribute__((aligned(1024))) unsigned char lds[Y::kBytes];
 
   const Geometry& G = a.g;
-  const int s = blockIdx.x;
-  const int kv = blockIdx.y / a.row_blocks;
-  const int rb = blockIdx.y % a.row_blocks;
-  const int b = blockIdx.z;
+  // Workgroups are dealt to the 8 XCDs round-robin in launch order.  When the grid divides
+  // evenly, launch index L runs unit (L % 8) * (N / 8) + L / 8, so the consecutive units of one
+  // (sequence, KV head) -- all its splits -- share an XCD and its L2 (their queries are read
+  // once per XCD).  The mapping is a permutation of the units; otherwise it is the identity.
+  int u = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  {
+    const int n = gridDim.x * gridDim.y * gridDim.z;
+    if (n % 8 == 0) u = (u % 8) * (n / 8) + u / 8;
+  }
+  const int s = u % gridDim.x;
+  const int kv = (u / gridDim.x) % gridDim.y / a.row_blocks;
+  const int rb = (u / gridDim.x) % gridDim.y % a.row_blocks;
+  const int b = u / (gridDim.x * gridDim.y);
   const int lane = threadIdx.x & 63;
   // wave-uniform by construction; readfirstlane lets the compiler see it (scalar branches)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
