@@ -50,7 +50,14 @@
  * accumulation, probabilities entering the PV product as fp16 and normalised by the sum of
  * those same rounded values, so a prefix part's log-sum-exp is within 2^-11 of the exact
  * one); HTA_F32 runs exact fp32 vector-ALU kernels meant for small validation shapes (same
- * plan, workspace and layouts).
+ * plan, workspace and layouts).  Range of bf16 values: the PV products of the prefix pass
+ * (and of hta_tree_partials) take V as fp16, so a prefix V value with |v| > 65504 -- legal in
+ * bf16 -- is not supported: it makes its chunk's partial non-finite, and the merge then
+ * writes every affected output row (out and lse) as NaN and records HTA_ERR_NONFINITE in the
+ * workspace status (read with hta_get_device_status).  V values below 2^-14 in magnitude
+ * enter as fp16 subnormals (absolute error at most 2^-25).  Any non-finite input (NaN/inf in
+ * q, k or v, padding past prefix_len excluded) is reported the same way.  The tree keys of
+ * hta_verify are exempt: its tree part runs in fp32.
  */
 #ifndef HTA_H
 #define HTA_H
@@ -72,7 +79,8 @@ typedef enum {
     HTA_ERR_TREE = 6,        /* (device) a parent pointer outside [-1, i-1] */
     HTA_ERR_PREFIX_LEN = 7,  /* (device) prefix_len[b] outside [0, max_prefix_len] */
     HTA_ERR_HIP = 8,         /* a HIP runtime call failed */
-    HTA_ERR_CACHE_FULL = 9   /* (device) prefix_len[b] + accepted nodes > max_prefix_len */
+    HTA_ERR_CACHE_FULL = 9,  /* (device) prefix_len[b] + accepted nodes > max_prefix_len */
+    HTA_ERR_NONFINITE = 10   /* (device) an output row came out non-finite and was NaN-filled */
 } hta_status;
 
 typedef enum { HTA_BF16 = 0, HTA_F32 = 1 } hta_dtype;
@@ -208,7 +216,8 @@ hta_status hta_chunk_mass(const hta_desc *desc, const int32_t *prefix_len, const
  * cache_len [B] (keys j < cache_len[b] are seen) -> out [B, Tq, Hq, D] float, lse [B, Hq, Tq].
  * Two launches: the split-K prefix pass and the merge of its partials (no tree part).  A
  * sequence with cache_len 0 gets out 0, lse -inf; a cache_len outside [0, Lmax] gives NaN
- * (no status word is written).
+ * (not recorded in the status); a non-finite output row is NaN-filled and recorded as
+ * HTA_ERR_NONFINITE in the workspace status, which this call clears first.
  */
 hta_status hta_cross_attention(const hta_desc *desc, const void *q, const void *k_cache,
                                const void *v_cache, const int32_t *cache_len, float *out,
@@ -351,10 +360,10 @@ hta_status hta_accept_commit(const hta_desc *desc, int32_t vocab, int32_t logits
 
 /*
  * Synchronise the stream, read the device status the last hta_verify / hta_tree_partials /
- * hta_ancestor_masks / hta_rope_tree / hta_accept_commit call left in the workspace, and
- * return HTA_OK, HTA_ERR_TREE, HTA_ERR_PREFIX_LEN or HTA_ERR_CACHE_FULL (reported in that
- * order of precedence).  *bad_sequence (if not NULL) receives the first offending batch
- * index, or -1.
+ * hta_ancestor_masks / hta_rope_tree / hta_accept_commit / hta_cross_attention call left in
+ * the workspace (hta_merge adds non-finite rows to it), and return HTA_OK, HTA_ERR_TREE,
+ * HTA_ERR_PREFIX_LEN, HTA_ERR_CACHE_FULL or HTA_ERR_NONFINITE (reported in that order of
+ * precedence).  *bad_sequence (if not NULL) receives the first offending batch index, or -1.
  */
 hta_status hta_get_device_status(const hta_desc *desc, const void *workspace, void *stream,
                                  int32_t *bad_sequence);

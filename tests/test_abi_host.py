@@ -284,3 +284,78 @@ def test_dense_mask_bytes_and_validation():
     q[5] = FAKE + 8
     assert L.hta_verify_dense(ctypes.byref(d), *q, None) == ALIGN
     assert L.hta_verify_dense(ctypes.byref(_desc(in_dtype=1)), *p, None) == DTYPE
+
+
+# ----------------------------------------------------------------------------- binding checks
+
+
+def _verify_tensors(B=2, T=5, Hq=8, Hkv=2, D=64, L=40, dtype=torch.bfloat16):
+    """Correctly shaped CPU tensors for hta_verify (the binding checks them before any call)."""
+    t = dict(q=torch.zeros(B, T, Hq, D, dtype=dtype),
+             k_prefix=torch.zeros(B, Hkv, L, D, dtype=dtype),
+             v_prefix=torch.zeros(B, Hkv, L, D, dtype=dtype),
+             k_tree=torch.zeros(B, Hkv, T, D, dtype=dtype),
+             v_tree=torch.zeros(B, Hkv, T, D, dtype=dtype),
+             parent_idx=torch.full((B, T), -1, dtype=torch.int32),
+             prefix_len=torch.full((B,), L, dtype=torch.int32),
+             out=torch.zeros(B, T, Hq, D, dtype=torch.float32),
+             lse=torch.zeros(B, Hq, T, dtype=torch.float32))
+    desc = hta.make_desc(B, Hq, Hkv, D, T, L, 0 if dtype == torch.bfloat16 else 1)
+    ws = torch.zeros(hta.workspace_size(desc), dtype=torch.uint8)
+    return desc, t, ws
+
+
+def _call_verify(desc, t, ws):
+    hta.hta_verify(desc, t["q"], t["k_prefix"], t["v_prefix"], t["k_tree"], t["v_tree"],
+                   t["parent_idx"], t["prefix_len"], t["out"], t["lse"], ws)
+
+
+@pytest.mark.parametrize("name,bad,exc", [
+    ("prefix_len", lambda t: t["prefix_len"].to(torch.int64), TypeError),
+    ("parent_idx", lambda t: t["parent_idx"].to(torch.int64), TypeError),
+    ("k_tree", lambda t: t["k_tree"].permute(0, 2, 1, 3).contiguous(), ValueError),
+    ("v_prefix", lambda t: t["v_prefix"][:, :, :-1].contiguous(), ValueError),
+    ("q", lambda t: t["q"].to(torch.float32), TypeError),
+    ("out", lambda t: t["out"].to(torch.bfloat16), TypeError),
+    ("lse", lambda t: t["lse"].transpose(1, 2), ValueError),
+    ("v_tree", lambda t: t["v_tree"].transpose(2, 3), ValueError),
+])
+def test_binding_rejects_mismatched_tensors(name, bad, exc):
+    """Every tensor the wrapper hands to the C ABI is checked against the descriptor first:
+    a wrong dtype, layout, length or stride is an error, never a misread on the device."""
+    desc, t, ws = _verify_tensors()
+    t[name] = bad(t)
+    with pytest.raises(exc, match=name):
+        _call_verify(desc, t, ws)
+
+
+def test_binding_rejects_small_workspace_and_host_tensors():
+    desc, t, ws = _verify_tensors()
+    with pytest.raises(ValueError, match="workspace"):
+        _call_verify(desc, t, ws[:-1])
+    with pytest.raises(TypeError, match="workspace"):
+        _call_verify(desc, t, ws.to(torch.int32))
+    # every shape and dtype right, but on the host: refused before the C call
+    with pytest.raises(ValueError, match="GPU"):
+        _call_verify(desc, t, ws)
+    with pytest.raises(ValueError, match="GPU"):
+        hta.prepare_verify(desc, t["q"], t["k_prefix"], t["v_prefix"], t["k_tree"], t["v_tree"],
+                           t["parent_idx"], t["prefix_len"], t["out"], t["lse"], ws)
+
+
+def test_binding_checks_the_other_wrappers():
+    desc, t, ws = _verify_tensors()
+    with pytest.raises(TypeError, match="prefix_len"):
+        hta.hta_prefix_partials(desc, t["q"], t["k_prefix"], t["v_prefix"],
+                                t["prefix_len"].to(torch.int64), ws)
+    with pytest.raises(ValueError, match="k_tree"):
+        hta.hta_tree_partials(desc, t["q"], t["k_tree"][:, :1].contiguous(), t["v_tree"],
+                              t["parent_idx"], t["prefix_len"], ws)
+    with pytest.raises(ValueError, match="out"):
+        hta.hta_merge(desc, t["prefix_len"], True, t["out"][:1].contiguous(), t["lse"], ws)
+    with pytest.raises(ValueError, match="k_cache"):
+        hta.hta_cross_attention(desc, t["q"], t["k_prefix"][:, :, :3].contiguous(),
+                                t["v_prefix"], t["prefix_len"], t["out"], t["lse"], ws)
+    with pytest.raises(ValueError, match="GPU"):
+        hta.hta_cross_attention(desc, t["q"], t["k_prefix"], t["v_prefix"], t["prefix_len"],
+                                t["out"], t["lse"], ws)

@@ -6,7 +6,9 @@ ancestor masks bit-exact.  Every input is seeded and synthetic (tree_verificatio
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import math
+import os
 import sys
 
 import numpy as np
@@ -60,10 +62,22 @@ def sample_rows(w: W.Workload, n: int, seed: int = 0):
     return b, h, i
 
 
+def oracle_rows(w: W.Workload, b, h, i, part=oracle.PART_ALL):
+    """The oracle's rows (b, h, i), spread over the host's cores (each row is the same
+    single-threaded C code; the C call releases the GIL)."""
+    arrs = w.as_numpy()
+    ncpu = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    threads = max(1, min(16, ncpu or 1, len(b) // 8 or 1))
+    idx = np.array_split(np.arange(len(b)), threads)
+    with cf.ThreadPoolExecutor(threads) as ex:
+        res = list(ex.map(lambda k: oracle.rows(arrs, w.scale, b[k], h[k], i[k], part), idx))
+    return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
+
+
 def check_rows(w: W.Workload, out, lse, n_rows: int = 10**9, seed: int = 0, part=oracle.PART_ALL,
                out_tol=OUT_TOL, lse_tol=LSE_TOL):
     b, h, i = sample_rows(w, n_rows, seed)
-    ro, rl = oracle.rows(w.as_numpy(), w.scale, b, h, i, part)
+    ro, rl = oracle_rows(w, b, h, i, part)
     go = out[b, i, h]
     gl = lse[b, h, i]
     if part == oracle.PART_PREFIX:

@@ -28,6 +28,7 @@ STATUS_NAMES = {
     7: "HTA_ERR_PREFIX_LEN",
     8: "HTA_ERR_HIP",
     9: "HTA_ERR_CACHE_FULL",
+    10: "HTA_ERR_NONFINITE",
 }
 EXPORTED = (
     "hta_plan",
@@ -209,27 +210,132 @@ def _contig(*ts: torch.Tensor) -> None:
             raise ValueError("all tensors must be contiguous")
 
 
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+_U8 = (torch.uint8,)
+
+
+def _in_dtype(desc: hta_desc):
+    return (torch.bfloat16,) if desc.in_dtype == HTA_BF16 else (torch.float32,)
+
+
+def _validate(specs, workspace: Optional[torch.Tensor] = None, ws_bytes: int = 0) -> None:
+    """Check every tensor a wrapper hands to the C ABI before the call: its dtype, shape and
+    contiguity against the descriptor (specs: (name, tensor, shape, dtypes), shape None = any),
+    then that all of them and the workspace (a 1-D uint8 buffer of at least ws_bytes) live on
+    one GPU.  The C ABI sees only pointers, so a mismatch here would otherwise be misread or
+    read out of bounds on the device."""
+    named = [x for x in specs if x[1] is not None]
+    if workspace is not None:
+        named.append(("workspace", workspace, None, _U8))
+    for name, t, shape, dtypes in named:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+        if t.dtype not in dtypes:
+            want = " or ".join(str(d) for d in dtypes)
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {want}")
+        if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if workspace is not None:
+        if workspace.dim() != 1 or workspace.numel() < ws_bytes:
+            raise ValueError(f"workspace must be a 1-D uint8 buffer of at least {ws_bytes} bytes,"
+                             f" got shape {tuple(workspace.shape)}")
+    dev = named[0][1].device
+    for name, t, _, _ in named:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} is on {t.device}: every tensor must be on a GPU")
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, {named[0][0]} on {dev}")
+
+
+def _dims(desc: hta_desc):
+    return (desc.batch, desc.tree_size, desc.num_q_heads, desc.num_kv_heads, desc.head_dim,
+            desc.max_prefix_len)
+
+
 # ----------------------------------------------------------------------------- entry points
 
 
 def hta_verify(desc, q, k_prefix, v_prefix, k_tree, v_tree, parent_idx, prefix_len, out, lse,
                workspace, stream=None) -> None:
-    _contig(q, k_prefix, v_prefix, k_tree, v_tree, parent_idx, prefix_len, out, lse, workspace)
+    B, T, Hq, Hkv, D, L = _dims(desc)
+    X = _in_dtype(desc)
+    _validate([("q", q, (B, T, Hq, D), X), ("k_prefix", k_prefix, (B, Hkv, L, D), X),
+               ("v_prefix", v_prefix, (B, Hkv, L, D), X), ("k_tree", k_tree, (B, Hkv, T, D), X),
+               ("v_tree", v_tree, (B, Hkv, T, D), X), ("parent_idx", parent_idx, (B, T), _I32),
+               ("prefix_len", prefix_len, (B,), _I32), ("out", out, (B, T, Hq, D), _F32),
+               ("lse", lse, (B, Hq, T), _F32)], workspace, workspace_size(desc))
     _check(load().hta_verify(ctypes.byref(desc), _ptr(q), _ptr(k_prefix), _ptr(v_prefix),
                              _ptr(k_tree), _ptr(v_tree), _ptr(parent_idx), _ptr(prefix_len),
                              _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                              _stream(stream)), "hta_verify")
 
 
+def prepare_verify(desc, q, k_prefix, v_prefix, k_tree, v_tree, parent_idx, prefix_len, out,
+                   lse, workspace, stream=None):
+    """hta_verify with its arguments checked and marshalled once: returns a callable that
+    enqueues the same call again (for loops that repeat one step on fixed buffers, where the
+    per-call checks would cost more host time than the GPU spends on the step)."""
+    B, T, Hq, Hkv, D, L = _dims(desc)
+    X = _in_dtype(desc)
+    _validate([("q", q, (B, T, Hq, D), X), ("k_prefix", k_prefix, (B, Hkv, L, D), X),
+               ("v_prefix", v_prefix, (B, Hkv, L, D), X), ("k_tree", k_tree, (B, Hkv, T, D), X),
+               ("v_tree", v_tree, (B, Hkv, T, D), X), ("parent_idx", parent_idx, (B, T), _I32),
+               ("prefix_len", prefix_len, (B,), _I32), ("out", out, (B, T, Hq, D), _F32),
+               ("lse", lse, (B, Hq, T), _F32)], workspace, workspace_size(desc))
+    fn = load().hta_verify
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k_prefix), _ptr(v_prefix), _ptr(k_tree),
+            _ptr(v_tree), _ptr(parent_idx), _ptr(prefix_len), _ptr(out), _ptr(lse),
+            _ptr(workspace), workspace.numel(), _stream(stream))
+    keep = (desc, q, k_prefix, v_prefix, k_tree, v_tree, parent_idx, prefix_len, out, lse,
+            workspace)
+
+    def call() -> None:
+        code = fn(*args)
+        if code != 0:
+            raise HtaError(code, "hta_verify")
+    call.keep = keep  # the buffers stay alive as long as the call
+    return call
+
+
+def prepare_prefix_partials(desc, q, k_prefix, v_prefix, prefix_len, workspace, stream=None):
+    """hta_prefix_partials checked and marshalled once (see prepare_verify)."""
+    B, T, Hq, Hkv, D, L = _dims(desc)
+    X = _in_dtype(desc)
+    _validate([("q", q, (B, T, Hq, D), X), ("k_prefix", k_prefix, (B, Hkv, L, D), X),
+               ("v_prefix", v_prefix, (B, Hkv, L, D), X), ("prefix_len", prefix_len, (B,), _I32)],
+              workspace, workspace_size(desc))
+    fn = load().hta_prefix_partials
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k_prefix), _ptr(v_prefix), _ptr(prefix_len),
+            _ptr(workspace), workspace.numel(), _stream(stream))
+    keep = (desc, q, k_prefix, v_prefix, prefix_len, workspace)
+
+    def call() -> None:
+        code = fn(*args)
+        if code != 0:
+            raise HtaError(code, "hta_prefix_partials")
+    call.keep = keep
+    return call
+
+
 def hta_ancestor_masks(desc, parent_idx, masks, workspace, stream=None) -> None:
-    _contig(parent_idx, masks, workspace)
+    B, T = desc.batch, desc.tree_size
+    _validate([("parent_idx", parent_idx, (B, T), _I32),
+               ("masks", masks, (B, T, (T + 63) // 64), (torch.int64,))],
+              workspace, workspace_size(desc))
     _check(load().hta_ancestor_masks(ctypes.byref(desc), _ptr(parent_idx), _ptr(masks),
                                      _ptr(workspace), workspace.numel(), _stream(stream)),
            "hta_ancestor_masks")
 
 
 def hta_prefix_partials(desc, q, k_prefix, v_prefix, prefix_len, workspace, stream=None) -> None:
-    _contig(q, k_prefix, v_prefix, prefix_len, workspace)
+    B, T, Hq, Hkv, D, L = _dims(desc)
+    X = _in_dtype(desc)
+    _validate([("q", q, (B, T, Hq, D), X), ("k_prefix", k_prefix, (B, Hkv, L, D), X),
+               ("v_prefix", v_prefix, (B, Hkv, L, D), X), ("prefix_len", prefix_len, (B,), _I32)],
+              workspace, workspace_size(desc))
     _check(load().hta_prefix_partials(ctypes.byref(desc), _ptr(q), _ptr(k_prefix),
                                       _ptr(v_prefix), _ptr(prefix_len), _ptr(workspace),
                                       workspace.numel(), _stream(stream)),
@@ -238,14 +344,20 @@ def hta_prefix_partials(desc, q, k_prefix, v_prefix, prefix_len, workspace, stre
 
 def hta_tree_partials(desc, q, k_tree, v_tree, parent_idx, prefix_len, workspace,
                       stream=None) -> None:
-    _contig(q, k_tree, v_tree, parent_idx, prefix_len, workspace)
+    B, T, Hq, Hkv, D, L = _dims(desc)
+    X = _in_dtype(desc)
+    _validate([("q", q, (B, T, Hq, D), X), ("k_tree", k_tree, (B, Hkv, T, D), X),
+               ("v_tree", v_tree, (B, Hkv, T, D), X), ("parent_idx", parent_idx, (B, T), _I32),
+               ("prefix_len", prefix_len, (B,), _I32)], workspace, workspace_size(desc))
     _check(load().hta_tree_partials(ctypes.byref(desc), _ptr(q), _ptr(k_tree), _ptr(v_tree),
                                     _ptr(parent_idx), _ptr(prefix_len), _ptr(workspace),
                                     workspace.numel(), _stream(stream)), "hta_tree_partials")
 
 
 def hta_merge(desc, prefix_len, include_tree: bool, out, lse, workspace, stream=None) -> None:
-    _contig(prefix_len, out, lse, workspace)
+    B, T, Hq, Hkv, D, L = _dims(desc)
+    _validate([("prefix_len", prefix_len, (B,), _I32), ("out", out, (B, T, Hq, D), _F32),
+               ("lse", lse, (B, Hq, T), _F32)], workspace, workspace_size(desc))
     _check(load().hta_merge(ctypes.byref(desc), _ptr(prefix_len), 1 if include_tree else 0,
                             _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                             _stream(stream)), "hta_merge")
@@ -259,9 +371,11 @@ def hta_get_device_status(desc, workspace, stream=None) -> Tuple[int, int]:
 
 
 def hta_chunk_mass(desc, prefix_len, lse, mass, chunk_scores, workspace, stream=None) -> None:
-    _contig(prefix_len, lse, mass, workspace)
-    if chunk_scores is not None:
-        _contig(chunk_scores)
+    B, T, Hq, Hkv, D, L = _dims(desc)
+    S1 = plan(desc).num_splits + 1
+    _validate([("prefix_len", prefix_len, (B,), _I32), ("lse", lse, (B, Hq, T), _F32),
+               ("mass", mass, (B, Hq, T, S1), _F32),
+               ("chunk_scores", chunk_scores, (B, S1), _F32)], workspace, workspace_size(desc))
     _check(load().hta_chunk_mass(ctypes.byref(desc), _ptr(prefix_len), _ptr(lse), _ptr(mass),
                                  _ptr(chunk_scores), _ptr(workspace), workspace.numel(),
                                  _stream(stream)), "hta_chunk_mass")
@@ -269,7 +383,12 @@ def hta_chunk_mass(desc, prefix_len, lse, mass, chunk_scores, workspace, stream=
 
 def hta_cross_attention(desc, q, k_cache, v_cache, cache_len, out, lse, workspace,
                         stream=None) -> None:
-    _contig(q, k_cache, v_cache, cache_len, out, lse, workspace)
+    B, T, Hq, Hkv, D, L = _dims(desc)
+    X = _in_dtype(desc)
+    _validate([("q", q, (B, T, Hq, D), X), ("k_cache", k_cache, (B, Hkv, L, D), X),
+               ("v_cache", v_cache, (B, Hkv, L, D), X), ("cache_len", cache_len, (B,), _I32),
+               ("out", out, (B, T, Hq, D), _F32), ("lse", lse, (B, Hq, T), _F32)],
+              workspace, workspace_size(desc))
     _check(load().hta_cross_attention(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                       _ptr(cache_len), _ptr(out), _ptr(lse), _ptr(workspace),
                                       workspace.numel(), _stream(stream)), "hta_cross_attention")
@@ -291,7 +410,12 @@ def cross_attention(q, k_cache, v_cache, cache_len, *, scale=None, chunk: int = 
 
 def hta_window_commit(desc, window: int, k_win, v_win, k_tree, v_tree, accepted, accept_len,
                       win_pos, workspace, stream=None) -> None:
-    _contig(k_win, v_win, k_tree, v_tree, accepted, accept_len, win_pos, workspace)
+    B, T, Hq, Hkv, D, L = _dims(desc)
+    X = _in_dtype(desc)
+    _validate([("k_win", k_win, (B, Hkv, window, D), X), ("v_win", v_win, (B, Hkv, window, D), X),
+               ("k_tree", k_tree, (B, Hkv, T, D), X), ("v_tree", v_tree, (B, Hkv, T, D), X),
+               ("accepted", accepted, (B, T), _I32), ("accept_len", accept_len, (B,), _I32),
+               ("win_pos", win_pos, (B,), _I32)], workspace, 4 * B)
     _check(load().hta_window_commit(ctypes.byref(desc), int(window), _ptr(k_win), _ptr(v_win),
                                     _ptr(k_tree), _ptr(v_tree), _ptr(accepted),
                                     _ptr(accept_len), _ptr(win_pos), _ptr(workspace),
@@ -309,7 +433,9 @@ def dense_mask_shape(desc: hta_desc) -> Tuple[int, int, int]:
 
 
 def hta_dense_mask(desc, parent_idx, prefix_len, mask, workspace, stream=None) -> None:
-    _contig(parent_idx, prefix_len, mask, workspace)
+    B, T = desc.batch, desc.tree_size
+    _validate([("parent_idx", parent_idx, (B, T), _I32), ("prefix_len", prefix_len, (B,), _I32),
+               ("mask", mask, dense_mask_shape(desc), (torch.int64,))], workspace, 4 * B)
     _check(load().hta_dense_mask(ctypes.byref(desc), _ptr(parent_idx), _ptr(prefix_len),
                                  _ptr(mask), _ptr(workspace), workspace.numel(),
                                  _stream(stream)), "hta_dense_mask")
@@ -317,7 +443,14 @@ def hta_dense_mask(desc, parent_idx, prefix_len, mask, workspace, stream=None) -
 
 def hta_verify_dense(desc, q, k_prefix, v_prefix, k_tree, v_tree, mask, prefix_len, out, lse,
                      stream=None) -> None:
-    _contig(q, k_prefix, v_prefix, k_tree, v_tree, mask, prefix_len, out, lse)
+    B, T, Hq, Hkv, D, L = _dims(desc)
+    X = _in_dtype(desc)
+    _validate([("q", q, (B, T, Hq, D), X), ("k_prefix", k_prefix, (B, Hkv, L, D), X),
+               ("v_prefix", v_prefix, (B, Hkv, L, D), X), ("k_tree", k_tree, (B, Hkv, T, D), X),
+               ("v_tree", v_tree, (B, Hkv, T, D), X),
+               ("mask", mask, dense_mask_shape(desc), (torch.int64,)),
+               ("prefix_len", prefix_len, (B,), _I32), ("out", out, (B, T, Hq, D), _F32),
+               ("lse", lse, (B, Hq, T), _F32)])
     _check(load().hta_verify_dense(ctypes.byref(desc), _ptr(q), _ptr(k_prefix), _ptr(v_prefix),
                                    _ptr(k_tree), _ptr(v_tree), _ptr(mask), _ptr(prefix_len),
                                    _ptr(out), _ptr(lse), _stream(stream)), "hta_verify_dense")
@@ -356,9 +489,11 @@ def chunk_mass(desc, prefix_len, lse, workspace, stream=None):
 
 def hta_rope_tree(desc, rope_theta: float, interleaved: bool, q, k_tree, parent_idx, prefix_len,
                   positions, workspace, stream=None) -> None:
-    _contig(q, k_tree, parent_idx, prefix_len, workspace)
-    if positions is not None:
-        _contig(positions)
+    B, T, Hq, Hkv, D, L = _dims(desc)
+    X = _in_dtype(desc)
+    _validate([("q", q, (B, T, Hq, D), X), ("k_tree", k_tree, (B, Hkv, T, D), X),
+               ("parent_idx", parent_idx, (B, T), _I32), ("prefix_len", prefix_len, (B,), _I32),
+               ("positions", positions, (B, T), _I32)], workspace, 4 * B)
     _check(load().hta_rope_tree(ctypes.byref(desc), float(rope_theta), 1 if interleaved else 0,
                                 _ptr(q), _ptr(k_tree), _ptr(parent_idx), _ptr(prefix_len),
                                 _ptr(positions), _ptr(workspace), workspace.numel(),
@@ -372,9 +507,17 @@ def accept_workspace_size(desc: hta_desc, vocab: int) -> int:
 def hta_accept_commit(desc, logits, tokens, root_token, parent_idx, prefix_len, k_prefix,
                       v_prefix, k_tree, v_tree, target_next, accept_len, accepted, bonus_token,
                       workspace, stream=None) -> None:
-    _contig(logits, tokens, root_token, parent_idx, prefix_len, k_prefix, v_prefix, k_tree,
-            v_tree, target_next, accept_len, accepted, bonus_token, workspace)
-    vocab = logits.shape[-1]
+    B, T, Hq, Hkv, D, L = _dims(desc)
+    X = _in_dtype(desc)
+    vocab = logits.shape[-1] if isinstance(logits, torch.Tensor) and logits.dim() == 3 else 0
+    _validate([("logits", logits, (B, T, vocab), (torch.bfloat16, torch.float32)),
+               ("tokens", tokens, (B, T), _I32), ("root_token", root_token, (B,), _I32),
+               ("parent_idx", parent_idx, (B, T), _I32), ("prefix_len", prefix_len, (B,), _I32),
+               ("k_prefix", k_prefix, (B, Hkv, L, D), X), ("v_prefix", v_prefix, (B, Hkv, L, D), X),
+               ("k_tree", k_tree, (B, Hkv, T, D), X), ("v_tree", v_tree, (B, Hkv, T, D), X),
+               ("target_next", target_next, (B, T), _I32), ("accept_len", accept_len, (B,), _I32),
+               ("accepted", accepted, (B, T), _I32), ("bonus_token", bonus_token, (B,), _I32)],
+              workspace, accept_workspace_size(desc, max(vocab, 1)))
     _check(load().hta_accept_commit(ctypes.byref(desc), int(vocab), _dtype_code(logits),
                                     _ptr(logits), _ptr(tokens), _ptr(root_token),
                                     _ptr(parent_idx), _ptr(prefix_len), _ptr(k_prefix),

@@ -99,6 +99,7 @@ Workspace carve(void* base, const hta_plan_info& p) {
   w.masks = (uint64_t*)(c + p.masks_offset);
   w.lse_part = (float*)(c + p.lse_part_offset);
   w.o_part = (uint32_t*)(c + p.o_part_offset);
+  w.status_reset = nullptr;
   return w;
 }
 
@@ -158,7 +159,8 @@ hta_status hta_verify(const hta_desc* desc, const void* q, const void* k_prefix,
   HTA_TRY(check_ptrs({q, k_tree, v_tree, parent_idx, prefix_len, out, lse}));
   if (G.Lmax > 0) HTA_TRY(check_ptrs({k_prefix, v_prefix}));  // an empty cache is never read
   HTA_TRY(check_ws(p, workspace, workspace_bytes));
-  const Workspace ws = carve(workspace, p);
+  Workspace ws = carve(workspace, p);
+  ws.status_reset = ws.status;  // the merge ORs this call's verdicts into cleared words
   hipStream_t s = (hipStream_t)stream;
   // two launches: the split-K prefix pass, then the merge with the tree part fused in
   HTA_TRY(hip_status(launch_prefix(G, q, k_prefix, v_prefix, prefix_len, ws, s)));
@@ -272,10 +274,10 @@ hta_status hta_cross_attention(const hta_desc* desc, const void* q, const void* 
   HTA_TRY(check_ptrs({q, cache_len, out, lse}));
   if (G.Lmax > 0) HTA_TRY(check_ptrs({k_cache, v_cache}));
   HTA_TRY(check_ws(p, workspace, workspace_bytes));
-  const Workspace ws = carve(workspace, p);
+  Workspace ws = carve(workspace, p);
+  ws.status_reset = ws.status;  // the merge ORs non-finite rows into cleared words
   hipStream_t s = (hipStream_t)stream;
-  // the prefix pass, then the merge of the prefix partials alone (no tree part); the merge
-  // reads no status word when the tree partial is left out
+  // the prefix pass, then the merge of the prefix partials alone (no tree part)
   HTA_TRY(hip_status(launch_prefix(G, q, k_cache, v_cache, cache_len, ws, s)));
   return hip_status(hta::launch_lse_merge(G, cache_len, false, out, lse, ws, s));
 }
@@ -401,7 +403,8 @@ hta_status hta_get_device_status(const hta_desc* desc, const void* workspace, vo
   hipStream_t s = (hipStream_t)stream;
   int32_t host_status[1024];
   hta_status first_tree = HTA_OK, first_len = HTA_OK, first_full = HTA_OK;
-  int32_t bad_tree = -1, bad_len = -1, bad_full = -1;
+  hta_status first_nonfinite = HTA_OK;
+  int32_t bad_tree = -1, bad_len = -1, bad_full = -1, bad_nonfinite = -1;
   for (int b0 = 0; b0 < G.B; b0 += 1024) {
     const int n = G.B - b0 < 1024 ? G.B - b0 : 1024;
     const char* src = (const char*)workspace + p.status_offset + sizeof(int32_t) * (size_t)b0;
@@ -422,6 +425,10 @@ hta_status hta_get_device_status(const hta_desc* desc, const void* workspace, vo
         first_full = HTA_ERR_CACHE_FULL;
         bad_full = b0 + k;
       }
+      if ((host_status[k] & hta::kStatusNonFinite) && first_nonfinite == HTA_OK) {
+        first_nonfinite = HTA_ERR_NONFINITE;
+        bad_nonfinite = b0 + k;
+      }
     }
   }
   if (first_tree != HTA_OK) {
@@ -435,6 +442,10 @@ hta_status hta_get_device_status(const hta_desc* desc, const void* workspace, vo
   if (first_full != HTA_OK) {
     if (bad_sequence) *bad_sequence = bad_full;
     return first_full;
+  }
+  if (first_nonfinite != HTA_OK) {
+    if (bad_sequence) *bad_sequence = bad_nonfinite;
+    return first_nonfinite;
   }
   return HTA_OK;
 }
@@ -452,6 +463,9 @@ const char* hta_status_str(hta_status status) {
     case HTA_ERR_HIP: return "HTA_ERR_HIP: a HIP runtime call failed";
     case HTA_ERR_CACHE_FULL:
       return "HTA_ERR_CACHE_FULL: the accepted path does not fit the prefix cache";
+    case HTA_ERR_NONFINITE:
+      return "HTA_ERR_NONFINITE: an output row came out non-finite (an input outside the "
+             "supported range, e.g. |v| > 65504 with bf16 inputs); the row was written as NaN";
   }
   return "HTA_ERR_UNKNOWN";
 }

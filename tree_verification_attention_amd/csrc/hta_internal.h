@@ -24,6 +24,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int32_t kStatusTree = 1;       // a parent pointer outside [-1, i-1]
 constexpr int32_t kStatusPrefixLen = 2;  // prefix_len[b] outside [0, Lmax]
 constexpr int32_t kStatusCacheFull = 4;  // the accepted path does not fit the prefix cache
+constexpr int32_t kStatusNonFinite = 8;  // an output row came out non-finite (e.g. a bf16 V
+                                         // value outside the fp16 range of the PV product)
 
 // Geometry shared by every kernel of one call (a plain struct passed by value).
 struct Geometry {
@@ -44,6 +46,9 @@ struct Workspace {
   uint64_t* masks;      // [B, T, W]
   float* lse_part;      // [B, Hkv, S+1, R_pad]
   uint32_t* o_part;     // [B, Hkv, S+1, R_pad, D] packed 24-bit values: 3 D / 4 dwords a row
+  // When set (== status), the prefix pass clears the status words first: a call whose later
+  // launch records bits with atomic ORs starts from zero.  nullptr leaves them alone.
+  int32_t* status_reset;
 };
 
 // Split-K partial outputs travel through memory as packed 24-bit floats: the top 24 bits of

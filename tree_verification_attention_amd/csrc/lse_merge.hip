@@ -29,6 +29,11 @@
 // and weighted value sum in fp32.  This replaces a launch and the partial round trip
 // through HBM with a few dozen dot products per row.  The fused merge also records the
 // sequence's device status.
+//
+// Both forms check every output row they write: a row that comes out non-finite (an input
+// outside what the prefix pass supports, such as a bf16 V value beyond the fp16 range of its
+// PV product, or a non-finite input) is written as NaN and recorded in the sequence's status
+// (kStatusNonFinite), so such a result is never silently wrong.
 #include "hta_internal.h"
 
 namespace hta {
@@ -42,6 +47,9 @@ constexpr int kMaxT = 256;
 struct MergeArgs {
   const int32_t* prefix_len;
   const int32_t* status;   // [B]: read by the plain merge (the tree pass status)
+  int32_t* status_or;      // [B]: non-finite rows (both forms) and, fused, the tree verdict
+                           // are OR-ed in (the call cleared the words first, or the tree pass
+                           // wrote them)
   float* lse_part;               // read by the merges, written by the tree-only form
   uint32_t* o_part;              // packed 24-bit rows (load24 / store24)
   float* out;
@@ -51,7 +59,6 @@ struct MergeArgs {
   const void* k_tree;            // [B, Hkv, T, D]
   const void* v_tree;
   const int32_t* parent_idx;     // [B, T]
-  int32_t* status_out;           // [B]
   Geometry g;
   int32_t include_tree;
 };
@@ -260,7 +267,8 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   load_parts(kEarly, kBatch);
   if (MODE == kFused && i == 0 && h == 0 && lane == 0) {  // the sequence's device status
     const bool len_bad = Lb < 0 || Lb > G.Lmax;
-    a.status_out[b] = (tree_bad ? kStatusTree : 0) | (len_bad ? kStatusPrefixLen : 0);
+    const int32_t bits = (tree_bad ? kStatusTree : 0) | (len_bad ? kStatusPrefixLen : 0);
+    if (bits) atomicOr(a.status_or + b, bits);
   }
   if constexpr (FUSED) {
     if (!tree_bad) batch(my0, k0, v0);
@@ -378,13 +386,26 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
     for (int e = 0; e < DPL; ++e) acc[e] += wt * group_sum4(at[e]);
   }
   const float inv = 1.f / wsum;
+  const float lse_row = Mn + __log2f(wsum) * kLn2;
+  bool finite = __builtin_isfinite(lse_row);
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    acc[e] *= inv;
+    finite = finite && __builtin_isfinite(acc[e]);
+  }
+  // a non-finite value anywhere in the row: the whole row is NaN and the status records it
+  const bool row_bad = __builtin_amdgcn_ballot_w64(!finite) != 0;
   if (pg == 0) {
 #pragma unroll
     for (int j = 0; j < NV; ++j)
-      ((float4*)outp)[j] = make_float4(acc[4 * j] * inv, acc[4 * j + 1] * inv,
-                                       acc[4 * j + 2] * inv, acc[4 * j + 3] * inv);
+      ((float4*)outp)[j] = row_bad ? make_float4(NAN, NAN, NAN, NAN)
+                                   : make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2],
+                                                 acc[4 * j + 3]);
   }
-  if (lane == 0) *lsep = Mn + __log2f(wsum) * kLn2;
+  if (lane == 0) {
+    *lsep = row_bad ? NAN : lse_row;
+    if (row_bad) atomicOr(a.status_or + b, kStatusNonFinite);
+  }
 }
 
 template <int MODE, typename TIN>
@@ -416,7 +437,7 @@ hipError_t launch_tree_mode(const Geometry& g, const void* q, const void* k_tree
   a.k_tree = k_tree;
   a.v_tree = v_tree;
   a.parent_idx = parent_idx;
-  a.status_out = ws.status;
+  a.status_or = ws.status;
   a.g = g;
   a.include_tree = 1;
   return g.f32 ? launch_merge<MODE, float>(a, g, stream)
@@ -430,6 +451,7 @@ hipError_t launch_lse_merge(const Geometry& g, const int32_t* prefix_len, bool i
   MergeArgs a = {};
   a.prefix_len = prefix_len;
   a.status = ws.status;  // read always, used only with the tree partial
+  a.status_or = ws.status;
   a.lse_part = ws.lse_part;
   a.o_part = ws.o_part;
   a.out = out;

@@ -25,6 +25,7 @@ struct PrefixF32Args {
   const float* k_prefix;    // [B, Hkv, Lmax, D]
   const float* v_prefix;
   const int32_t* prefix_len;
+  int32_t* status_reset;  // [B] or nullptr: cleared by the first workgroup of b
   float* lse_part;
   uint32_t* o_part;  // packed 24-bit rows (store24)
   Geometry g;
@@ -48,6 +49,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefix_attn_f32(PrefixF32Args a) 
   const Geometry& G = a.g;
   const int s = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (a.status_reset && s == 0 && kv == 0 && threadIdx.x == 0) a.status_reset[b] = 0;
   int Lb = a.prefix_len[b];
   Lb = Lb < 0 ? 0 : (Lb > G.Lmax ? G.Lmax : Lb);  // out-of-range lengths are flagged elsewhere
   const int kbeg = s * G.chunk;
@@ -120,6 +122,7 @@ hipError_t launch_prefix_attn_f32(const Geometry& g, const void* q, const void* 
   a.k_prefix = (const float*)k_prefix;
   a.v_prefix = (const float*)v_prefix;
   a.prefix_len = prefix_len;
+  a.status_reset = ws.status_reset;
   a.lse_part = ws.lse_part;
   a.o_part = ws.o_part;
   a.g = g;

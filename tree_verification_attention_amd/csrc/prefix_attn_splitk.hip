@@ -146,6 +146,7 @@ struct PrefixArgs {
   const unsigned short* k_prefix;  // [B, Hkv, Lmax, D]
   const unsigned short* v_prefix;
   const int32_t* prefix_len;       // [B]
+  int32_t* status_reset;           // [B] or nullptr: cleared by the first workgroup of b
   float* lse_part;
   uint32_t* o_part;                // packed 24-bit rows (store24)
   Geometry g;
@@ -199,6 +200,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   const int l16 = lane & 15;
   const int grp = lane >> 4;
 
+  if (a.status_reset && s == 0 && kv == 0 && rb == 0 && threadIdx.x == 0) a.status_reset[b] = 0;
   int Lb = a.prefix_len[b];
   Lb = Lb < 0 ? 0 : (Lb > G.Lmax ? G.Lmax : Lb);  // out-of-range lengths are flagged elsewhere
   const int kbeg = s * G.chunk;
@@ -799,6 +801,7 @@ hipError_t launch_prefix_attn_splitk(const Geometry& g, const void* q, const voi
   a.k_prefix = (const unsigned short*)k_prefix;
   a.v_prefix = (const unsigned short*)v_prefix;
   a.prefix_len = prefix_len;
+  a.status_reset = ws.status_reset;
   a.lse_part = ws.lse_part;
   a.o_part = ws.o_part;
   a.g = g;
