@@ -80,7 +80,8 @@ typedef enum {
     HTA_ERR_PREFIX_LEN = 7,  /* (device) prefix_len[b] outside [0, max_prefix_len] */
     HTA_ERR_HIP = 8,         /* a HIP runtime call failed */
     HTA_ERR_CACHE_FULL = 9,  /* (device) prefix_len[b] + accepted nodes > max_prefix_len */
-    HTA_ERR_NONFINITE = 10   /* (device) an output row came out non-finite and was NaN-filled */
+    HTA_ERR_NONFINITE = 10,  /* (device) an output row came out non-finite and was NaN-filled */
+    HTA_ERR_SCRATCH = 11     /* hta_verify_noalloc: the plan needs more than its static scratch */
 } hta_status;
 
 typedef enum { HTA_BF16 = 0, HTA_F32 = 1 } hta_dtype;
@@ -144,6 +145,26 @@ hta_status hta_verify(const hta_desc *desc, const void *q, const void *k_prefix,
                       const void *v_prefix, const void *k_tree, const void *v_tree,
                       const int32_t *parent_idx, const int32_t *prefix_len, float *out,
                       float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * hta_verify without a workspace argument and without any allocation, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same launches, results bit-identical to hta_verify.
+ * The workspace is a static device array inside the library, HTA_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) per GPU, held by every GPU the library runs on until the process ends; a
+ * descriptor whose hta_workspace_size() exceeds it is refused with HTA_ERR_SCRATCH before
+ * anything is enqueued.  Every call on one GPU shares that GPU's scratch: calls that overlap
+ * on one GPU (different streams, threads) race and must be ordered by the caller.  status
+ * (device int32 [B], may be NULL) receives the per-sequence device verdicts that
+ * hta_get_device_status would report, as OR-ed flags (1: invalid tree, 2: prefix_len out of
+ * range, 8: a non-finite row); with NULL they stay in the scratch, and the affected rows are
+ * NaN either way.  The first call on a device looks up the scratch's address (no allocation).
+ */
+#define HTA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+hta_status hta_verify_noalloc(const hta_desc *desc, const void *q, const void *k_prefix,
+                              const void *v_prefix, const void *k_tree, const void *v_tree,
+                              const int32_t *parent_idx, const int32_t *prefix_len, float *out,
+                              float *lse, int32_t *status, void *stream);
 
 /*
  * Ancestor-or-self masks of every draft tree (the tree mask of README, Introduction),

@@ -359,3 +359,18 @@ def test_binding_checks_the_other_wrappers():
     with pytest.raises(ValueError, match="GPU"):
         hta.hta_cross_attention(desc, t["q"], t["k_prefix"], t["v_prefix"], t["prefix_len"],
                                 t["out"], t["lse"], ws)
+
+
+def test_noalloc_refuses_plans_beyond_its_scratch():
+    """The allocation-free entry point checks the plan against its static scratch first."""
+    L = hta.load()
+    big = _desc(batch=64, max_prefix_len=262144)
+    assert hta.workspace_size(big) > (64 << 20)
+    fake = [16 * (i + 1) for i in range(10)]
+    code = L.hta_verify_noalloc(ctypes.byref(big), *fake, None, None)
+    assert code == 11 and hta.status_str(code).startswith("HTA_ERR_SCRATCH")
+    # a plan that fits gets as far as the pointer checks (nothing dereferenced or launched)
+    small = _desc()
+    assert hta.workspace_size(small) <= (64 << 20)
+    assert L.hta_verify_noalloc(ctypes.byref(small), None, *fake[1:], None, None) == NULL
+    assert L.hta_verify_noalloc(ctypes.byref(small), *fake[:9], 8, None, None) == ALIGN

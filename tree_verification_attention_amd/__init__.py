@@ -27,6 +27,7 @@ from .binding import (  # noqa: F401
     hta_tree_partials,
     hta_verify,
     hta_verify_dense,
+    hta_verify_noalloc,
     hta_window_commit,
     load,
     make_desc,
@@ -47,7 +48,7 @@ __all__ = [
     "cross_attention", "dense_mask_shape", "desc_for", "hta_cross_attention",
     "hta_window_commit", "hta_accept_commit", "hta_ancestor_masks", "hta_chunk_mass",
     "hta_dense_mask", "hta_verify_dense", "verify_dense", "hta_get_device_status", "hta_merge",
-    "hta_prefix_partials", "hta_rope_tree", "hta_tree_partials", "hta_verify", "load",
+    "hta_prefix_partials", "hta_rope_tree", "hta_tree_partials", "hta_verify", "hta_verify_noalloc", "load",
     "make_desc", "new_workspace", "partial_views", "plan", "prepare_prefix_partials",
     "prepare_verify", "rope_tree", "status_str", "verify",
     "workspace_size",

@@ -29,11 +29,13 @@ STATUS_NAMES = {
     8: "HTA_ERR_HIP",
     9: "HTA_ERR_CACHE_FULL",
     10: "HTA_ERR_NONFINITE",
+    11: "HTA_ERR_SCRATCH",
 }
 EXPORTED = (
     "hta_plan",
     "hta_workspace_size",
     "hta_verify",
+    "hta_verify_noalloc",
     "hta_ancestor_masks",
     "hta_prefix_partials",
     "hta_tree_partials",
@@ -107,6 +109,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.hta_workspace_size.argtypes = [D]
     L.hta_workspace_size.restype = S
     L.hta_verify.argtypes = [D, P, P, P, P, P, P, P, P, P, P, S, P]
+    L.hta_verify_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P]
     L.hta_ancestor_masks.argtypes = [D, P, P, P, S, P]
     L.hta_prefix_partials.argtypes = [D, P, P, P, P, P, S, P]
     L.hta_tree_partials.argtypes = [D, P, P, P, P, P, P, S, P]
@@ -126,7 +129,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.hta_status_str.argtypes = [ctypes.c_int]
     L.hta_status_str.restype = ctypes.c_char_p
     L.hta_version.argtypes = []
-    for f in (L.hta_plan, L.hta_verify, L.hta_ancestor_masks, L.hta_prefix_partials,
+    for f in (L.hta_plan, L.hta_verify, L.hta_verify_noalloc, L.hta_ancestor_masks, L.hta_prefix_partials,
               L.hta_tree_partials, L.hta_merge, L.hta_get_device_status, L.hta_version,
               L.hta_rope_tree, L.hta_accept_commit, L.hta_chunk_mass, L.hta_dense_mask,
               L.hta_verify_dense, L.hta_cross_attention, L.hta_window_commit):
@@ -271,6 +274,23 @@ def hta_verify(desc, q, k_prefix, v_prefix, k_tree, v_tree, parent_idx, prefix_l
                              _ptr(k_tree), _ptr(v_tree), _ptr(parent_idx), _ptr(prefix_len),
                              _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                              _stream(stream)), "hta_verify")
+
+
+def hta_verify_noalloc(desc, q, k_prefix, v_prefix, k_tree, v_tree, parent_idx, prefix_len,
+                       out, lse, status=None, stream=None) -> None:
+    """hta_verify on the library's static scratch: no workspace, nothing allocated.  status
+    (int32 [B] on the device, optional) receives the per-sequence device flags."""
+    B, T, Hq, Hkv, D, L = _dims(desc)
+    X = _in_dtype(desc)
+    _validate([("q", q, (B, T, Hq, D), X), ("k_prefix", k_prefix, (B, Hkv, L, D), X),
+               ("v_prefix", v_prefix, (B, Hkv, L, D), X), ("k_tree", k_tree, (B, Hkv, T, D), X),
+               ("v_tree", v_tree, (B, Hkv, T, D), X), ("parent_idx", parent_idx, (B, T), _I32),
+               ("prefix_len", prefix_len, (B,), _I32), ("out", out, (B, T, Hq, D), _F32),
+               ("lse", lse, (B, Hq, T), _F32), ("status", status, (B,), _I32)])
+    _check(load().hta_verify_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_prefix),
+                                     _ptr(v_prefix), _ptr(k_tree), _ptr(v_tree),
+                                     _ptr(parent_idx), _ptr(prefix_len), _ptr(out), _ptr(lse),
+                                     _ptr(status), _stream(stream)), "hta_verify_noalloc")
 
 
 def prepare_verify(desc, q, k_prefix, v_prefix, k_tree, v_tree, parent_idx, prefix_len, out,

@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/hta.h"
 #include "hta_internal.h"
 
@@ -128,6 +130,34 @@ hipError_t launch_prefix(const Geometry& G, const void* q, const void* k_prefix,
                : hta::launch_prefix_attn_splitk(G, q, k_prefix, v_prefix, prefix_len, ws, s);
 }
 
+// ---- the allocation-free entry point's scratch
+//
+// hta_verify_noalloc serves callers that cannot allocate (code under HIP graph capture,
+// tight serving loops): its workspace is this file-scope device array instead of a buffer
+// the caller hands in.  Each GPU the library runs on holds its own copy until the process
+// ends.  In host code `scratch` names a host-side stand-in, not device memory, so its
+// device address is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is ever passed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (looked up on the first call on that device).
+hta_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HTA_ERR_HIP;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // (two threads racing here both find the same address)
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HTA_ERR_HIP;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return HTA_OK;
+}
+
 #define HTA_TRY(expr)                  \
   do {                                 \
     hta_status _s = (expr);            \
@@ -163,6 +193,29 @@ hta_status hta_verify(const hta_desc* desc, const void* q, const void* k_prefix,
   ws.status_reset = ws.status;  // the merge ORs this call's verdicts into cleared words
   hipStream_t s = (hipStream_t)stream;
   // two launches: the split-K prefix pass, then the merge with the tree part fused in
+  HTA_TRY(hip_status(launch_prefix(G, q, k_prefix, v_prefix, prefix_len, ws, s)));
+  return hip_status(hta::launch_tree_merge(G, q, k_tree, v_tree, parent_idx, prefix_len, out,
+                                           lse, ws, s));
+}
+
+hta_status hta_verify_noalloc(const hta_desc* desc, const void* q, const void* k_prefix,
+                              const void* v_prefix, const void* k_tree, const void* v_tree,
+                              const int32_t* parent_idx, const int32_t* prefix_len, float* out,
+                              float* lse, int32_t* status, void* stream) {
+  Geometry G;
+  hta_plan_info p;
+  HTA_TRY(make_plan(desc, &G, &p));
+  if (p.workspace_bytes > kScratchBytes) return HTA_ERR_SCRATCH;
+  HTA_TRY(check_ptrs({q, k_tree, v_tree, parent_idx, prefix_len, out, lse}));
+  if (G.Lmax > 0) HTA_TRY(check_ptrs({k_prefix, v_prefix}));
+  if (status && !aligned16(status)) return HTA_ERR_ALIGN;
+  void* base = nullptr;
+  HTA_TRY(scratch_for_current_device(&base));
+  Workspace ws = carve(base, p);
+  if (status) ws.status = status;  // the caller reads the verdicts from its own buffer
+  ws.status_reset = ws.status;     // cleared by the prefix pass, OR-ed by the merge
+  hipStream_t s = (hipStream_t)stream;
+  // the same two launches as hta_verify, on the static scratch
   HTA_TRY(hip_status(launch_prefix(G, q, k_prefix, v_prefix, prefix_len, ws, s)));
   return hip_status(hta::launch_tree_merge(G, q, k_tree, v_tree, parent_idx, prefix_len, out,
                                            lse, ws, s));
@@ -463,6 +516,9 @@ const char* hta_status_str(hta_status status) {
     case HTA_ERR_HIP: return "HTA_ERR_HIP: a HIP runtime call failed";
     case HTA_ERR_CACHE_FULL:
       return "HTA_ERR_CACHE_FULL: the accepted path does not fit the prefix cache";
+    case HTA_ERR_SCRATCH:
+      return "HTA_ERR_SCRATCH: hta_verify_noalloc needs more scratch than its static 64 MiB "
+             "(hta_workspace_size() of the descriptor is larger); use hta_verify";
     case HTA_ERR_NONFINITE:
       return "HTA_ERR_NONFINITE: an output row came out non-finite (an input outside the "
              "supported range, e.g. |v| > 65504 with bf16 inputs); the row was written as NaN";
