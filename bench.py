@@ -44,6 +44,67 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+def settle(fn, seconds: float) -> int:
+    """Call fn until `seconds` of wall time have passed, so the engine clock has reached its
+    steady state under this load before anything is timed.  Returns the calls made."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(20):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n
+
+
+def time_loop(fn, n: int, stream):
+    """n calls of fn timed two ways at once: wall clock between device synchronisations, and
+    HIP events recorded on the launch stream around the same calls.  µs per call each."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for k in range(n):
+        fn(k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / n * 1e6
+    return wall, e0.elapsed_time(e1) / n * 1e3
+
+
+def kv_rotation(w: W.Workload, dev):
+    """The prefix cache on the device plus copies, so that consecutive calls together touch at
+    least ROTATE_BYTES (more than the 256 MB Infinity Cache) and time HBM."""
+    kv_copy_bytes = w.k_prefix.numel() * w.k_prefix.element_size() * 2
+    n_copies = max(1, min(64, math.ceil(ROTATE_BYTES / kv_copy_bytes)))
+    kp0, vp0 = w.k_prefix.to(dev), w.v_prefix.to(dev)
+    kps = [kp0] + [kp0.clone() for _ in range(n_copies - 1)]
+    vps = [vp0] + [vp0.clone() for _ in range(n_copies - 1)]
+    return kps, vps, n_copies, kv_copy_bytes
+
+
+def roofline_figures(fig: dict, step_us: float, prefix_us: float) -> dict:
+    """Achieved rates of a step against the published peaks; the bound is whichever of the
+    HBM time and the matrix-core time of the algorithmic work is longer."""
+    t_hbm = fig["step_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = fig["step_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    gbs = fig["step_bytes"] / (step_us * 1e-6) / 1e9
+    tfs = fig["step_flops"] / (step_us * 1e-6) / 1e12
+    return {
+        "us_per_step": round(step_us, 3),
+        "prefix_us": round(prefix_us, 3),
+        "alg_bytes": fig["step_bytes"], "alg_flops": fig["step_flops"],
+        "GBps": round(gbs, 1), "TFLOPs": round(tfs, 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4),
+        "bound": "mfma" if t_mfma > t_hbm else "hbm",
+        "roofline_us": round(max(t_hbm, t_mfma) * 1e6, 3),
+        "roofline_frac": round(max(t_hbm, t_mfma) / (step_us * 1e-6), 4),
+        "prefix_GBps": round(fig["prefix_bytes"] / (prefix_us * 1e-6) / 1e9, 1),
+        "prefix_TFLOPs": round(fig["prefix_flops"] / (prefix_us * 1e-6) / 1e12, 1),
+    }
+
+
 def alg_figures(w: W.Workload):
     """Algorithmic bytes and flops of one step and of the prefix kernel alone.
 
@@ -177,8 +238,11 @@ def cpu_baseline(w: W.Workload, max_seconds: float = 12.0):
     t0 = time.perf_counter()
     o1, l1 = oracle.rows(a, w.scale, b, h, i)
     dt1 = time.perf_counter() - t0
-    threads = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
-                         else (os.cpu_count() or 1)))
+    # every core this process may run on, up to the 16-core host share one GPU has on the
+    # benchmark machines (their rule for worker pools)
+    allowed = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    host_cores = os.cpu_count() or 1
+    threads = max(1, min(16, allowed or host_cores))
     parts = np.array_split(np.arange(n), threads)
     t0 = time.perf_counter()
     with cf.ThreadPoolExecutor(threads) as ex:  # the C call releases the GIL
@@ -196,9 +260,109 @@ def cpu_baseline(w: W.Workload, max_seconds: float = 12.0):
             "sample": f"{n} of {total} query rows (b, head, node) of the same workload, fp64 C "
                       f"oracle, rows spread over {threads} threads ({dtn:.1f} s), scaled to the "
                       f"full step",
+            "host_cores": host_cores, "cores_allowed": allowed,
+            "threads_note": "threads = the cores this process may use, capped at the 16-core "
+                            "host share of one GPU on the benchmark machines",
             "single_thread_value": dt1 / n * total * 1e6,
             "bitwise_equal_across_threads": bool(np.array_equal(o1, on) and np.array_equal(l1, ln)),
             "cpu_model": cpu}
+
+
+# The configurations of the pages' evaluation besides the headline: the 262k-context Llama-3
+# checkpoint, Vicuna-7B at batch 8 with ragged prefixes, and the QwQ-32B long-reasoning sweep
+# on the LongSpec tree and on a 5-token chain.
+OTHER_CONFIGS = ("llama3_8b_256k", "vicuna7b_b8",
+                 "qwq32b_tree_4k", "qwq32b_tree_8k", "qwq32b_tree_16k", "qwq32b_tree_32k",
+                 "qwq32b_chain5_4k", "qwq32b_chain5_8k", "qwq32b_chain5_16k",
+                 "qwq32b_chain5_32k")
+
+
+def bench_config(name: str, dev, stream, settle_s: float = 0.25, target_s: float = 0.2) -> dict:
+    """One configuration: its step (hta_verify) and its prefix pass alone, timed like the
+    headline (clock settled, warm-up, then wall clock and HIP events over the same calls),
+    with the step's algorithmic bytes and flops against both peaks."""
+    w = W.by_name(name)
+    fig = alg_figures(w)
+    B, T, Hq, D = w.q.shape
+    q = w.q.to(dev)
+    kt, vt = w.k_tree.to(dev), w.v_tree.to(dev)
+    par, plen = w.parent_idx.to(dev), w.prefix_len.to(dev)
+    kps, vps, n_copies, _ = kv_rotation(w, dev)
+    desc = hta.desc_for(q, kps[0], w.scale)
+    info = hta.plan(desc)
+    ws = hta.new_workspace(desc, dev)
+    out = torch.empty(B, T, Hq, D, dtype=torch.float32, device=dev)
+    lse = torch.empty(B, Hq, T, dtype=torch.float32, device=dev)
+    steps = [hta.prepare_verify(desc, q, kps[c], vps[c], kt, vt, par, plen, out, lse, ws, stream)
+             for c in range(n_copies)]
+    pres = [hta.prepare_prefix_partials(desc, q, kps[c], vps[c], plen, ws, stream)
+            for c in range(n_copies)]
+    t0 = time.perf_counter()
+    n_settle = settle(lambda k: steps[k % n_copies](), settle_s)
+    per_call = (time.perf_counter() - t0) / n_settle
+    code, _ = hta.hta_get_device_status(desc, ws, stream)
+    if code != 0:
+        raise RuntimeError(f"{name}: device status {hta.status_str(code)}")
+    n = int(min(2000, max(50, target_s / per_call)))
+    wall, ev = time_loop(lambda k: steps[k % n_copies](), n, stream)
+    for k in range(50):
+        pres[k % n_copies]()
+    _, pre = time_loop(lambda k: pres[k % n_copies](), n, stream)
+    rec = roofline_figures(fig, wall, pre)
+    rec.update({
+        "events_us": round(ev, 3), "steps_timed": n,
+        "batch": B, "num_q_heads": Hq, "num_kv_heads": w.num_kv_heads, "tree_nodes": T,
+        "prefix_len_sum": int(w.prefix_len.sum()), "prefix_len_max": int(w.prefix_len.max()),
+        "chunk": info.chunk, "splits": info.num_splits, "kv_copies_rotated": n_copies,
+    })
+    log(f"[bench] {name}: {wall:.2f} us/step (events {ev:.2f}), prefix {pre:.2f} us, "
+        f"{rec['GBps']:.0f} GB/s, {rec['TFLOPs']:.0f} TFLOP/s, {rec['bound']}-bound, "
+        f"roofline {rec['roofline_frac']:.3f}")
+    del steps, pres, kps, vps, q, kt, vt, par, plen, ws, out, lse, w
+    torch.cuda.empty_cache()
+    return rec
+
+
+def summarize_trace(run_dir: str, workload: str, command: str) -> str:
+    """A kernel-trace summary (rocprofv3 --kernel-trace --stats) of a --mode step-only run as a
+    markdown table under profiles/: calls, average, min, max and share per kernel."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {run_dir}")
+    rows = []
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+                         float(r["Percentage"])))
+    rows.sort(key=lambda x: -x[5])
+    w = W.by_name(workload)
+    fig = alg_figures(w)
+    whole = "--mode step-only" not in command
+    title = (f"the whole bench.py run on {workload} (headline, kernels alone, baselines, other "
+             f"configurations)" if whole else f"one verification step per call, {workload}")
+    lines = [f"# Kernel trace: {title}", "",
+             "Command (from the repository root, on one MI355X):", "", "```",
+             "cd /tmp && export TMPDIR=/tmp && cd - && " + command, "```", "",
+             f"Workload: batch {w.batch}, {w.num_q_heads} query / {w.num_kv_heads} KV heads, "
+             f"head_dim {w.head_dim}, {w.tree_size} tree nodes, prefix lengths summing to "
+             f"{int(w.prefix_len.sum())} (max {int(w.prefix_len.max())}).  Algorithmic bytes "
+             f"per step {fig['step_bytes']}, flops {fig['step_flops']}.  Counts include "
+             "the clock-settling and warm-up launches; the copies are the rotated prefix caches "
+             "being made.", "",
+             "| Kernel | Calls | Average (us) | Min (us) | Max (us) | Share |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for name, calls, avg, mn, mx, pct in rows:
+        short = name.replace("hta::(anonymous namespace)::", "").replace("void ", "")
+        short = short.split("(")[0] if not short.startswith("__amd") else short
+        lines.append(f"| `{short}` | {calls} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {pct:.1f}% |")
+    out = os.path.join(PROFILE_DIR, f"{'bench' if whole else 'verify_step'}_{workload}"
+                                    "_kernel_stats.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return out
 
 
 def measured_peaks(dev) -> dict:
@@ -314,7 +478,9 @@ def bench_around(w: W.Workload, dev, stream, steps: int, warmup: int) -> dict:
         "accept_commit_frac_of_hbm_peak": round(logits_bytes / (accept_us * 1e-6) / 1e9
                                                 / HBM_PEAK_GBS, 4),
         "note": "accept_commit = the vocabulary argmax launch plus the acceptance/commit "
-                "launch; the kernel trace splits the two",
+                "launch; the kernel trace splits the two.  These loops call the unprepared "
+                "wrappers, whose per-call host time exceeds these kernels' device time, so "
+                "the figures are host-paced; the kernel trace has the device times",
     }
 
 
@@ -381,8 +547,17 @@ def main() -> int:
     ap.add_argument("--workload", default="llama3_8b_32k", choices=W.CONFIG_NAMES)
     ap.add_argument("--chunk", type=int, default=0, help="split-K chunk (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="bench", choices=["bench", "prefix-only", "copy"],
-                    help="prefix-only / copy: launch only that kernel (for counter runs)")
+    ap.add_argument("--mode", default="bench", choices=["bench", "prefix-only", "step-only",
+                                                         "copy"],
+                    help="prefix-only / step-only / copy: launch only that (for profiler runs)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other configurations (the configs object)")
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed steps before the warm-up, so the engine clock is "
+                         "at its steady state under this load")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "COMMAND"),
+                    help="write a kernel-trace summary of --workload from a rocprofv3 "
+                         "--kernel-trace --stats output folder into profiles/ and exit")
     ap.add_argument("--summarize-counters", nargs=4, metavar="DIR",
                     help="write the prefix kernel's HBM traffic from four rocprofv3 --pmc "
                          "output folders (FETCH_SIZE, WRITE_SIZE, then the same for --mode "
@@ -391,6 +566,9 @@ def main() -> int:
 
     if args.summarize_counters:
         print(summarize_counters(args.workload, *args.summarize_counters))
+        return 0
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace[0], args.workload, args.summarize_trace[1]))
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -420,15 +598,11 @@ def main() -> int:
     w = W.by_name(args.workload)
     fig = alg_figures(w)
     B, T, Hq, D = w.q.shape
-    kv_copy_bytes = w.k_prefix.numel() * w.k_prefix.element_size() * 2
-    n_copies = max(1, min(16, math.ceil(ROTATE_BYTES / kv_copy_bytes)))
     q = w.q.to(dev)
     kt, vt = w.k_tree.to(dev), w.v_tree.to(dev)
     par, plen = w.parent_idx.to(dev), w.prefix_len.to(dev)
-    kp0, vp0 = w.k_prefix.to(dev), w.v_prefix.to(dev)
-    kps = [kp0] + [kp0.clone() for _ in range(n_copies - 1)]
-    vps = [vp0] + [vp0.clone() for _ in range(n_copies - 1)]
-    desc = hta.desc_for(q, kp0, w.scale, args.chunk)
+    kps, vps, n_copies, kv_copy_bytes = kv_rotation(w, dev)
+    desc = hta.desc_for(q, kps[0], w.scale, args.chunk)
     info = hta.plan(desc)
     ws = hta.new_workspace(desc, dev)
     out = torch.empty(B, T, Hq, D, dtype=torch.float32, device=dev)
@@ -450,41 +624,37 @@ def main() -> int:
     def prefix_only(k):
         prefix_calls[k % n_copies]()
 
-    if args.mode == "prefix-only":
+    if args.mode in ("prefix-only", "step-only"):
+        fn = prefix_only if args.mode == "prefix-only" else step
+        if args.mode == "step-only":  # (not under counter collection: too slow there)
+            settle(fn, args.settle)
         for k in range(args.warmup + args.steps):
-            prefix_only(k)
+            fn(k)
         torch.cuda.synchronize()
-        print(json.dumps({"mode": "prefix-only", "workload": args.workload,
+        print(json.dumps({"mode": args.mode, "workload": args.workload,
                           "launches": args.warmup + args.steps,
                           "alg_bytes_per_launch": fig["prefix_bytes"]}))
         return 0
 
-    # ---- whole step
+    # ---- whole step: clock settled, W warm-up steps, then exactly K timed steps, each loop
+    # bracketed by device synchronisations; wall clock (the headline) and HIP events on the
+    # launch stream measure the same K calls
+    settle_calls = settle(step, args.settle)
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
     code, _ = hta.hta_get_device_status(desc, ws, stream)
     if code != 0:
         raise RuntimeError(f"device status {hta.status_str(code)}")
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(k)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    us_per_step = wall / args.steps * 1e6
-    log(f"[bench] step: {us_per_step:.2f} us")
-
-    # the same steps timed with HIP events on the launch stream (GPU time only)
+    us_per_step, step_events_us = time_loop(step, args.steps, stream)
+    log(f"[bench] step: {us_per_step:.2f} us wall clock, {step_events_us:.2f} us HIP events "
+        f"({settle_calls} settle + {args.warmup} warm-up steps first)")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for k in range(args.steps):
-        step(k)
-    e1.record(stream)
-    e1.synchronize()
-    step_events_us = e0.elapsed_time(e1) / args.steps * 1e3
-    log(f"[bench] step (HIP events): {step_events_us:.2f} us")
+    # secondary loops (kernels alone, the spread of single calls) run at least this many
+    # calls, each after a warm-up of its own
+    n_side = max(args.steps, 200)
     # each call between its own event pair: the spread of single steps
-    n_calls = min(args.steps, 200)
+    n_calls = n_side
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n_calls)]
     for k, (a0, a1) in enumerate(evs):
@@ -497,32 +667,30 @@ def main() -> int:
     log(f"[bench] single steps: p10 {p10:.2f} p50 {p50:.2f} p90 {p90:.2f} us")
 
     # ---- dominant kernel alone, HIP events on the launch stream
-    for k in range(args.warmup):
+    for k in range(max(args.warmup, 50)):
         prefix_only(k)
-    e0.record(stream)
-    for k in range(args.steps):
-        prefix_only(k)
-    e1.record(stream)
-    e1.synchronize()
-    prefix_us = e0.elapsed_time(e1) / args.steps * 1e3
+    _, prefix_us = time_loop(prefix_only, n_side, stream)
     achieved_gbs = fig["prefix_bytes"] / (prefix_us * 1e-6) / 1e9
     achieved_tflops = fig["prefix_flops"] / (prefix_us * 1e-6) / 1e12
     log(f"[bench] prefix_attn_splitk: {prefix_us:.2f} us, {achieved_gbs:.0f} GB/s, "
         f"{achieved_tflops:.0f} TFLOP/s")
 
-    # ---- the other two kernels alone (context for the step time)
-    e0.record(stream)
-    for k in range(args.steps):
-        hta.hta_tree_partials(desc, q, kt, vt, par, plen, ws, stream)
-    e1.record(stream)
-    e1.synchronize()
-    tree_us = e0.elapsed_time(e1) / args.steps * 1e3
-    e0.record(stream)
-    for k in range(args.steps):
-        hta.hta_merge(desc, plen, True, out, lse, ws, stream)
-    e1.record(stream)
-    e1.synchronize()
-    merge_us = e0.elapsed_time(e1) / args.steps * 1e3
+    # ---- the other two kernels alone (context for the step time), each warmed up first
+    tree_call = hta.prepare_tree_partials(desc, q, kt, vt, par, plen, ws, stream)
+    merge_call = hta.prepare_merge(desc, plen, True, out, lse, ws, stream)
+
+    def tree_only(k):
+        tree_call()
+
+    def merge_only(k):
+        merge_call()
+
+    for k in range(50):
+        tree_only(k)
+    _, tree_us = time_loop(tree_only, n_side, stream)
+    for k in range(50):
+        merge_only(k)
+    _, merge_us = time_loop(merge_only, n_side, stream)
     log(f"[bench] tree_attn_masked: {tree_us:.2f} us, lse_merge: {merge_us:.2f} us")
 
     result = {
@@ -551,7 +719,13 @@ def main() -> int:
             "roofline_frac": round(max(fig["step_bytes"] / (HBM_PEAK_GBS * 1e9),
                                        fig["step_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12))
                                    / (us_per_step * 1e-6), 4),
+            "wall_us": round(us_per_step, 3),
             "events_us": round(step_events_us, 3),
+            "settle_steps": settle_calls,
+            "timing_note": "value = wall clock over the K timed steps between device "
+                           "synchronisations; events_us = HIP events on the launch stream "
+                           "around the same K calls (GPU time, without the host's first-launch "
+                           "and final-synchronisation latency)",
             "per_call_us": {"p10": round(p10, 3), "p50": round(p50, 3), "p90": round(p90, 3),
                             "calls": n_calls},
             "kernel_us": {"prefix_attn_splitk": round(prefix_us, 3),
@@ -578,12 +752,8 @@ def main() -> int:
     step(0)
     for _ in range(50):
         hta.hta_chunk_mass(desc, plen, lse, mass, scores, ws, stream)
-    e0.record(stream)
-    for _ in range(args.steps):
-        hta.hta_chunk_mass(desc, plen, lse, mass, scores, ws, stream)
-    e1.record(stream)
-    e1.synchronize()
-    mass_us = e0.elapsed_time(e1) / args.steps * 1e3
+    _, mass_us = time_loop(lambda k: hta.hta_chunk_mass(desc, plen, lse, mass, scores, ws, stream),
+                           n_side, stream)
     log(f"[bench] chunk_mass: {mass_us:.2f} us")
     result["chunk_mass"] = {
         "us": round(mass_us, 3), "columns": info.num_splits + 1,
@@ -592,7 +762,7 @@ def main() -> int:
     # ---- the method's "before": one masked pass over all L + T keys, explicit mask
     dmask = torch.empty(hta.dense_mask_shape(desc), dtype=torch.int64, device=dev)
     hta.hta_dense_mask(desc, par, plen, dmask, ws, stream)
-    dense_steps = max(20, args.steps // 5)
+    dense_steps = max(20, n_side // 5)
     for k in range(20):
         hta.hta_verify_dense(desc, q, kps[k % n_copies], vps[k % n_copies], kt, vt, dmask, plen,
                              out, lse, stream)
@@ -611,21 +781,34 @@ def main() -> int:
     dmask_us = e0.elapsed_time(e1) / dense_steps * 1e3
     log(f"[bench] single-pass masked baseline: {dense_us:.1f} us (+ mask {dmask_us:.1f} us), "
         f"{(dense_us + dmask_us) / step_events_us:.2f}x the hybrid step")
+    dense_wgs = (info.rows_padded // 16 + 3) // 4 * w.num_kv_heads * B
     result["dense_masked_baseline"] = {
         "us": round(dense_us, 3), "mask_build_us": round(dmask_us, 3),
         "mask_bytes": int(dmask.numel() * 8), "launches_timed": dense_steps,
         "before_over_after": round((dense_us + dmask_us) / step_events_us, 3),
-        "note": "one masked pass over all L+T keys per (64 query rows, KV head), explicit "
-                "mask; before_over_after = (mask build + pass) / the hybrid step (HIP events)",
+        "workgroups": dense_wgs, "simds_busy": 4 * dense_wgs, "simds": 1024,
+        "note": f"one masked pass over all L+T keys per (64 query rows, KV head), explicit "
+                f"mask; before_over_after = (mask build + pass) / the hybrid step (HIP events). "
+                f"That pass runs {dense_wgs} workgroups of 4 waves ({4 * dense_wgs} of the "
+                f"1024 SIMDs) with no split over the keys, so the ratio also counts the "
+                f"parallelism the split-K prefix pass adds",
     }
-    result["drafter"] = bench_drafter(w, dev, stream, args.steps, kps, vps, n_copies)
-    result["around_attention"] = bench_around(w, dev, stream, args.steps, args.warmup)
+    result["drafter"] = bench_drafter(w, dev, stream, n_side, kps, vps, n_copies)
+    result["around_attention"] = bench_around(w, dev, stream, n_side, args.warmup)
     peaks = measured_peaks(dev)
     log(f"[bench] measured peaks: {peaks}")
     result["measured_peaks"] = peaks
     result["roofline"]["frac_of_measured_peak"] = round(achieved_gbs / peaks["hbm_copy_GBps"], 4)
     result["roofline"]["mfma"]["frac_of_measured_peak"] = round(
         achieved_tflops / peaks["bf16_gemm_TFLOPs"], 4)
+    # ---- the other configurations, each timed like the headline
+    del kps, vps
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        result["configs"] = {"llama3_8b_32k": roofline_figures(fig, us_per_step, prefix_us)}
+        result["configs"]["llama3_8b_32k"]["events_us"] = round(step_events_us, 3)
+        for name in OTHER_CONFIGS:
+            result["configs"][name] = bench_config(name, dev, stream)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w)

@@ -353,6 +353,11 @@ def test_binding_checks_the_other_wrappers():
                               t["parent_idx"], t["prefix_len"], ws)
     with pytest.raises(ValueError, match="out"):
         hta.hta_merge(desc, t["prefix_len"], True, t["out"][:1].contiguous(), t["lse"], ws)
+    with pytest.raises(ValueError, match="out"):
+        hta.prepare_merge(desc, t["prefix_len"], True, t["out"][:1].contiguous(), t["lse"], ws)
+    with pytest.raises(TypeError, match="parent_idx"):
+        hta.prepare_tree_partials(desc, t["q"], t["k_tree"], t["v_tree"],
+                                  t["parent_idx"].to(torch.int64), t["prefix_len"], ws)
     with pytest.raises(ValueError, match="k_cache"):
         hta.hta_cross_attention(desc, t["q"], t["k_prefix"][:, :, :3].contiguous(),
                                 t["v_prefix"], t["prefix_len"], t["out"], t["lse"], ws)

@@ -74,3 +74,38 @@ def test_tree_partial_matches_oracle(T, kind):
         torch.cuda.synchronize()
         assert hta.hta_get_device_status(desc, ws) == (0, -1)
         check_rows(w, out.cpu().double().numpy(), lse.cpu().double().numpy())
+
+
+def test_prepared_calls_match_direct_calls():
+    """The prepared (checked-once) tree, prefix and merge calls enqueue exactly what the direct
+    calls do: the unfused step through either path is bit-identical, also when repeated."""
+    B, Hkv, G, D, T = 2, 2, 4, 128, 68
+    w = W.make_workload("prepared", batch=B, num_q_heads=G * Hkv, num_kv_heads=Hkv,
+                        head_dim=D, max_prefix_len=700, prefix_len=[700, 321],
+                        tree_widths=W.LONGSPEC_TREE_WIDTHS, seed=77, peaky_frac=0.02,
+                        dtype=torch.bfloat16)
+    t = to_dev(w)
+    desc = hta.desc_for(t["q"], t["k_prefix"], w.scale, chunk=128)
+    res = []
+    for prepared in (False, True, True):
+        ws = hta.new_workspace(desc, "cuda")
+        out = torch.full((B, T, G * Hkv, D), float("nan"), device="cuda")
+        lse = torch.full((B, G * Hkv, T), float("nan"), device="cuda")
+        if prepared:
+            hta.prepare_tree_partials(desc, t["q"], t["k_tree"], t["v_tree"], t["parent_idx"],
+                                      t["prefix_len"], ws)()
+            hta.prepare_prefix_partials(desc, t["q"], t["k_prefix"], t["v_prefix"],
+                                        t["prefix_len"], ws)()
+            hta.prepare_merge(desc, t["prefix_len"], True, out, lse, ws)()
+        else:
+            hta.hta_tree_partials(desc, t["q"], t["k_tree"], t["v_tree"], t["parent_idx"],
+                                  t["prefix_len"], ws)
+            hta.hta_prefix_partials(desc, t["q"], t["k_prefix"], t["v_prefix"],
+                                    t["prefix_len"], ws)
+            hta.hta_merge(desc, t["prefix_len"], True, out, lse, ws)
+        torch.cuda.synchronize()
+        assert hta.hta_get_device_status(desc, ws) == (0, -1)
+        res.append((out.cpu(), lse.cpu()))
+    for o, l in res[1:]:
+        assert torch.equal(o, res[0][0]) and torch.equal(l, res[0][1])
+    check_rows(w, res[0][0].double().numpy(), res[0][1].double().numpy())

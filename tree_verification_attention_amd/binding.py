@@ -362,6 +362,45 @@ def hta_prefix_partials(desc, q, k_prefix, v_prefix, prefix_len, workspace, stre
            "hta_prefix_partials")
 
 
+def prepare_tree_partials(desc, q, k_tree, v_tree, parent_idx, prefix_len, workspace,
+                          stream=None):
+    """hta_tree_partials checked and marshalled once (see prepare_verify)."""
+    B, T, Hq, Hkv, D, L = _dims(desc)
+    X = _in_dtype(desc)
+    _validate([("q", q, (B, T, Hq, D), X), ("k_tree", k_tree, (B, Hkv, T, D), X),
+               ("v_tree", v_tree, (B, Hkv, T, D), X), ("parent_idx", parent_idx, (B, T), _I32),
+               ("prefix_len", prefix_len, (B,), _I32)], workspace, workspace_size(desc))
+    fn = load().hta_tree_partials
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(parent_idx),
+            _ptr(prefix_len), _ptr(workspace), workspace.numel(), _stream(stream))
+    keep = (desc, q, k_tree, v_tree, parent_idx, prefix_len, workspace)
+
+    def call() -> None:
+        code = fn(*args)
+        if code != 0:
+            raise HtaError(code, "hta_tree_partials")
+    call.keep = keep
+    return call
+
+
+def prepare_merge(desc, prefix_len, include_tree: bool, out, lse, workspace, stream=None):
+    """hta_merge checked and marshalled once (see prepare_verify)."""
+    B, T, Hq, Hkv, D, L = _dims(desc)
+    _validate([("prefix_len", prefix_len, (B,), _I32), ("out", out, (B, T, Hq, D), _F32),
+               ("lse", lse, (B, Hq, T), _F32)], workspace, workspace_size(desc))
+    fn = load().hta_merge
+    args = (ctypes.byref(desc), _ptr(prefix_len), 1 if include_tree else 0, _ptr(out),
+            _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream))
+    keep = (desc, prefix_len, out, lse, workspace)
+
+    def call() -> None:
+        code = fn(*args)
+        if code != 0:
+            raise HtaError(code, "hta_merge")
+    call.keep = keep
+    return call
+
+
 def hta_tree_partials(desc, q, k_tree, v_tree, parent_idx, prefix_len, workspace,
                       stream=None) -> None:
     B, T, Hq, Hkv, D, L = _dims(desc)
