@@ -81,7 +81,10 @@ typedef enum {
     HTA_ERR_HIP = 8,         /* a HIP runtime call failed */
     HTA_ERR_CACHE_FULL = 9,  /* (device) prefix_len[b] + accepted nodes > max_prefix_len */
     HTA_ERR_NONFINITE = 10,  /* (device) an output row came out non-finite and was NaN-filled */
-    HTA_ERR_SCRATCH = 11     /* hta_verify_noalloc: the plan needs more than its static scratch */
+    HTA_ERR_SCRATCH = 11,    /* hta_verify_noalloc: the plan needs more than its static scratch */
+    /* not a status: makes every int32_t value a valid hta_status, so hta_status_str() may be
+     * handed any code (unknown ones read "HTA_ERR_UNKNOWN") */
+    HTA_STATUS_MAX_ENUM = 0x7FFFFFFF
 } hta_status;
 
 typedef enum { HTA_BF16 = 0, HTA_F32 = 1 } hta_dtype;

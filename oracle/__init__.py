@@ -77,7 +77,11 @@ def configure(L: ctypes.CDLL) -> ctypes.CDLL:
 
 
 def lib() -> ctypes.CDLL:
+    """The oracle library: the in-tree build (rebuilt when a source is newer), or the build
+    HTA_ORACLE_LIBRARY names (e.g. one with sanitizers)."""
     global _lib
+    if _lib is None and os.environ.get("HTA_ORACLE_LIBRARY"):
+        _lib = configure(ctypes.CDLL(os.environ["HTA_ORACLE_LIBRARY"]))
     if _lib is None:
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(
                 os.path.getmtime(_SRC), os.path.getmtime(_SRC_STEP)):

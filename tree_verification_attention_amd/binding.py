@@ -93,11 +93,14 @@ class hta_plan_info(ctypes.Structure):
 _lib: Optional[ctypes.CDLL] = None
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libhta.so (raises if it is missing: the HIP path is the only path)."""
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libhta.so (raises if it is missing: the HIP path is the only path).  The path is
+    the in-tree build unless HTA_LIBRARY names another build of the same sources."""
     global _lib
     if _lib is not None:
         return _lib
+    if path is None:
+        path = os.environ.get("HTA_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise ImportError(
             f"{path} is missing: build it with `python -m tree_verification_attention_amd.build`"

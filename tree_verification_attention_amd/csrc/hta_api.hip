@@ -522,6 +522,7 @@ const char* hta_status_str(hta_status status) {
     case HTA_ERR_NONFINITE:
       return "HTA_ERR_NONFINITE: an output row came out non-finite (an input outside the "
              "supported range, e.g. |v| > 65504 with bf16 inputs); the row was written as NaN";
+    case HTA_STATUS_MAX_ENUM: break;
   }
   return "HTA_ERR_UNKNOWN";
 }
