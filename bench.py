@@ -268,6 +268,60 @@ def cpu_baseline(w: W.Workload, max_seconds: float = 12.0):
             "cpu_model": cpu}
 
 
+SQ_PASSES = (
+    "SQ_WAVE_CYCLES SQ_BUSY_CU_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS "
+    "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_VALU_MFMA_BUSY_CYCLES",
+    "SQ_ACTIVE_INST_ANY SQ_VALU_MFMA_COEXEC_CYCLES SQ_LDS_BANK_CONFLICT SQ_LDS_ADDR_CONFLICT "
+    "SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL SQ_INSTS_VALU SQ_INSTS_MFMA",
+    "SQ_CYCLES SQ_WAVES SQ_INSTS_LDS SQ_INSTS_SALU SQ_ACTIVE_INST_SCA SQ_ACTIVE_INST_VMEM "
+    "SQ_INST_LEVEL_LDS SQ_ACTIVE_INST_MISC",
+)
+
+
+def summarize_sq(workload: str, dirs) -> str:
+    """SQ counters of the prefix kernel from three rocprofv3 --pmc passes (SQ_PASSES, each on
+    --mode prefix-only) as a markdown table plus the per-wave and per-SIMD ratios."""
+    kern = "prefix_attn_splitk"
+    vals = {}
+    for d, counters in zip(dirs, SQ_PASSES):
+        for c in counters.split():
+            vals[c] = _counter_means(d, kern, c)[0]
+    waves = vals["SQ_WAVES"]
+    per = lambda c: vals[c] / waves  # noqa: E731
+    life = per("SQ_WAVE_CYCLES")
+    simds = 1024
+    mfma_busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
+    cmds = "\n".join(
+        f"rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- python3 bench.py "
+        f"--workload {workload} --mode prefix-only --steps 10 --warmup 2"
+        for d, c in zip(dirs, SQ_PASSES))
+    lines = [f"# SQ counters: prefix_attn_splitk, {workload}", "",
+             "Commands (from the repository root, on one MI355X; three passes of at most eight "
+             "SQ counters each), then `python3 bench.py --workload " + workload +
+             " --summarize-sq " + " ".join(dirs) + "`:", "", "```",
+             "cd /tmp && export TMPDIR=/tmp && cd -", cmds, "```", "",
+             f"Kernel source sha256[:16] = `{kernel_source_hash()}`.  Values: per dispatch, "
+             "summed over the chip's counter instances, averaged over the sampled dispatches.",
+             "", "| Counter | Per dispatch |", "|---|---:|"]
+    for c in sorted(vals):
+        lines.append(f"| `{c}` | {vals[c]:,.0f} |")
+    lines += ["",
+              f"Per wave ({waves:,.0f} waves; wave-cycle counters count 4-cycle units): lifetime "
+              f"{life:,.0f} units; issuing (ACTIVE_INST_ANY) {per('SQ_ACTIVE_INST_ANY') / life:.0%}, "
+              f"stalled on dependencies (WAIT_INST_ANY) {per('SQ_WAIT_INST_ANY') / life:.0%}, "
+              f"waiting at s_waitcnt / barriers (WAIT_ANY) {per('SQ_WAIT_ANY') / life:.0%}.  "
+              f"Matrix core: VALU_MFMA_BUSY {mfma_busy:,.0f} cycles per SIMD; VALU and MFMA "
+              f"co-execute in {vals['SQ_VALU_MFMA_COEXEC_CYCLES'] / vals['SQ_VALU_MFMA_BUSY_CYCLES']:.0%} "
+              f"of the MFMA-busy cycles.  Instructions per wave: {per('SQ_INSTS_MFMA'):,.0f} MFMA, "
+              f"{per('SQ_INSTS_VALU'):,.0f} VALU (MFMA included), {per('SQ_INSTS_LDS'):,.0f} LDS, "
+              f"{per('SQ_INSTS_SALU'):,.0f} SALU; LDS bank-conflict cycles "
+              f"{per('SQ_LDS_BANK_CONFLICT'):,.0f} per wave."]
+    out = os.path.join(PROFILE_DIR, f"prefix_attn_splitk_{workload}_sq_counters.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return out
+
+
 # The configurations of the pages' evaluation besides the headline: the 262k-context Llama-3
 # checkpoint, Vicuna-7B at batch 8 with ragged prefixes, and the QwQ-32B long-reasoning sweep
 # on the LongSpec tree and on a 5-token chain.
@@ -555,6 +609,9 @@ def main() -> int:
     ap.add_argument("--settle", type=float, default=0.5,
                     help="seconds of untimed steps before the warm-up, so the engine clock is "
                          "at its steady state under this load")
+    ap.add_argument("--summarize-sq", nargs=3, metavar="DIR",
+                    help="write the prefix kernel's SQ counters from the three rocprofv3 --pmc "
+                         "passes of SQ_PASSES into profiles/ and exit; needs no GPU")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "COMMAND"),
                     help="write a kernel-trace summary of --workload from a rocprofv3 "
                          "--kernel-trace --stats output folder into profiles/ and exit")
@@ -566,6 +623,9 @@ def main() -> int:
 
     if args.summarize_counters:
         print(summarize_counters(args.workload, *args.summarize_counters))
+        return 0
+    if args.summarize_sq:
+        print(summarize_sq(args.workload, args.summarize_sq))
         return 0
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace[0], args.workload, args.summarize_trace[1]))
