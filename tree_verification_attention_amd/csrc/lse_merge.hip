@@ -192,7 +192,9 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   load_parts(0, kEarly);
 
   // ---- validate
-  bool bad = Lb < 0 || Lb > G.Lmax || (tree_slot && st != 0);
+  // (only the tree pass's verdicts reject a sequence here: rows of this launch OR the
+  // non-finite flag into the same words while it runs)
+  bool bad = Lb < 0 || Lb > G.Lmax || (tree_slot && (st & (kStatusTree | kStatusPrefixLen)) != 0);
   bool tree_bad = false;  // the chain walk needs only this verdict, not the prefix length
   if constexpr (FUSED) {
     // parent pointers: parent[j] in [-1, j-1] for every node (the tree is topologically
