@@ -188,10 +188,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     const int n = gridDim.x * gridDim.y * gridDim.z;
     if (n % 8 == 0) u = (u % 8) * (n / 8) + u / 8;
   }
-  const int s = u % gridDim.x;
-  const int kv = (u / gridDim.x) % gridDim.y / a.row_blocks;
-  const int rb = (u / gridDim.x) % gridDim.y % a.row_blocks;
-  const int b = u / (gridDim.x * gridDim.y);
+  // (wave-uniform; readfirstlane keeps them, and the K/V addresses derived from them, in
+  // scalar registers, so each direct load is a scalar base plus one lane offset)
+  const int s = __builtin_amdgcn_readfirstlane(u % gridDim.x);
+  const int kv = __builtin_amdgcn_readfirstlane((u / gridDim.x) % gridDim.y / a.row_blocks);
+  const int rb = __builtin_amdgcn_readfirstlane((u / gridDim.x) % gridDim.y % a.row_blocks);
+  const int b = __builtin_amdgcn_readfirstlane(u / (gridDim.x * gridDim.y));
   const int lane = threadIdx.x & 63;
   // wave-uniform by construction; readfirstlane lets the compiler see it (scalar branches)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -577,16 +579,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
 #pragma unroll
           for (int db = 0; db < DB; ++db)
             accl[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[db], popl, accl[db], 0, 0, 0);
-        } else if (ljj == 0) {
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            accl[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                __builtin_shufflevector(vop[db], vop[db], 0, 1, 2, 3), popl4, accl[db], 0, 0, 0);
         } else {
+          // the K = 32 product over the whole half with P zero outside this wave's 16-key
+          // block (block ljj: the first or second 8-byte half of the operand).  The K = 16
+          // product would need a branch on ljj, and the compiler never updates that product's
+          // accumulators in place: it copied all of them back where the branches join.
+          const uint2 pb = __builtin_bit_cast(uint2, popl4);
+          const uint4 pz = ljj == 0 ? make_uint4(pb.x, pb.y, 0u, 0u) : make_uint4(0u, 0u, pb.x, pb.y);
+          const f16x8 p8 = __builtin_bit_cast(f16x8, pz);
 #pragma unroll
           for (int db = 0; db < DB; ++db)
-            accl[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                __builtin_shufflevector(vop[db], vop[db], 4, 5, 6, 7), popl4, accl[db], 0, 0, 0);
+            accl[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[db], p8, accl[db], 0, 0, 0);
         }
       }
     }
