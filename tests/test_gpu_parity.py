@@ -225,6 +225,22 @@ def test_verify_row_tilings(G, T):
         check_rows(w, out, lse, n_rows=3000)
 
 
+@pytest.mark.parametrize("T", [16, 19, 22, 25, 35, 38, 41, 44, 68])
+def test_verify_row_shapes_g5(T):
+    """Five query heads per KV head (T*G = 80 .. 340 rows, a ragged last tile each): every
+    split of 5 to 14 row tiles between the two wave groups, including second-group waves
+    with fewer tiles than first-group ones, and 22 tiles in two blocks of 11."""
+    G = 5
+    gen = torch.Generator().manual_seed(500 + T)
+    par = [W.random_forest(T, gen), W.level_tree((T // 3, T - T // 3), gen)]
+    w = _small(f"shapes_G5_T{T}", par, B=2, Hq=2 * G, Hkv=2, D=128, L=650, plen=[650, 301],
+               seed=500 + T)
+    _log(f"verify row shapes G=5 T={T} rows={T * G}")
+    for chunk in (192, 0):
+        out, lse = run_gpu(w, chunk=chunk)
+        check_rows(w, out, lse, n_rows=3000)
+
+
 @pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 130, 256])
 def test_verify_tree_sizes(T):
     gen = torch.Generator().manual_seed(T)

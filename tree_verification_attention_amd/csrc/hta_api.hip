@@ -53,15 +53,18 @@ hta_status make_plan(const hta_desc* d, Geometry* g, hta_plan_info* info) {
   G.W = (G.T + 63) / 64;
   G.scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)G.D);
   G.f32 = d->in_dtype == HTA_F32 ? 1 : 0;
-  int mt, tpb, nb;
-  hta::prefix_row_blocking(G, &mt, &tpb, &nb);
+  int tpb, nb;
+  hta::prefix_row_blocking(G, &tpb, &nb);
   const int64_t row_blocks = nb;
   int64_t chunk = d->chunk;
   if (chunk == 0) {
-    // Batches may be ragged (prefix_len varies); smaller chunks then balance the load.
+    // As many splits as keep every CU busy without a second partial wave of workgroups:
+    // S = CUs / (B * Hkv * row blocks), at least one.  Batches may be ragged (prefix_len
+    // varies); four workgroups per CU then balance the load.
     const int64_t waves = G.B > 1 ? 4 : 1;
-    const int64_t work = (int64_t)G.B * G.Hkv * row_blocks * (int64_t)G.Lmax;
-    chunk = (work + kPlanCUs * waves - 1) / (kPlanCUs * waves);
+    const int64_t units = (int64_t)G.B * G.Hkv * row_blocks;
+    const int64_t splits = units >= kPlanCUs * waves ? 1 : (kPlanCUs * waves) / units;
+    chunk = (G.Lmax + splits - 1) / splits;
     chunk = (chunk + 63) / 64 * 64;
     if (chunk < kMinChunk) chunk = kMinChunk;
     if (chunk > kMaxChunk) chunk = kMaxChunk;

@@ -163,8 +163,8 @@ hipError_t launch_dense_masked(const Geometry& g, const void* q, const void* k_p
                                const uint64_t* mask, const int32_t* prefix_len, float* out,
                                float* lse, hipStream_t stream);
 
-// How the prefix pass blocks the query rows of one KV head: mt full row tiles per wave,
-// tiles_per_block row tiles per workgroup, blocks workgroups per (sequence, KV head, chunk).
-void prefix_row_blocking(const Geometry& g, int* mt, int* tiles_per_block, int* blocks);
+// How the prefix pass blocks the query rows of one KV head: tiles_per_block row tiles per
+// workgroup, blocks workgroups per (sequence, KV head, chunk).
+void prefix_row_blocking(const Geometry& g, int* tiles_per_block, int* blocks);
 
 }  // namespace hta

@@ -22,10 +22,12 @@
 //    per SIMD).  A wave's own VALU work overlaps its matrix-core work poorly, but the VALU
 //    work of one wave overlaps the MFMAs of the other, so the two groups alternate between
 //    matrix-core phases and softmax phases half a phase pair apart (see run_chunk).  Each
-//    wave holds MT row tiles.  Leftover tiles (when the count is not a multiple of 8) go to
-//    the first group, split by keys: each of its waves covers some 16-key blocks of every
-//    tile for all D output dims, and the waves' partials are combined at the end.  The first
-//    group also issues the tile loads; the second builds V^T.
+//    first-group wave holds MT row tiles, each second-group wave MTB <= MT (fewer when the
+//    block's tiles do not fill both groups: the matrix core of a SIMD is shared by its two
+//    waves, so padding tiles would cost real products).  Leftover tiles go to the first
+//    group, split by keys: each of its waves covers some 16-key blocks of every tile for
+//    all D output dims, and the waves' partials are combined at the end.  The first group
+//    also issues the tile loads; the second builds V^T.
 //  * Memory: K and V tiles of 64 keys stream HBM -> LDS with direct LDS loads
 //    (global_load_lds_dwordx4, no register staging), two to three tiles in flight while
 //    one is consumed.  Rows land unpadded with an XOR swizzle of their 16-byte chunks so
@@ -155,19 +157,20 @@ struct PrefixArgs {
   float c;                         // scale * log2(e)
 };
 
-// MT full row tiles per wave (both wave groups); NL leftover tiles (0..2) per block, split
-// over the first wave group by keys.
-// What one call of the pass lambdas does: leftover keys (value) and own row tiles (rows).
-template <bool WL, bool ROWS>
+// What one call of the pass lambdas does: leftover keys (value) and the row tiles the
+// calling wave owns (rows).
+template <bool WL, int ROWS>
 struct PassTag {
   static constexpr bool value = WL;
-  static constexpr bool rows = ROWS;
+  static constexpr int rows = ROWS;
 };
 
-// BROWS: the second wave group owns row tiles.  With at most 4 row tiles per block the first
-// group holds them all and the second only builds V^T (no scores, softmax or PV of padding
-// rows on the SIMDs the first group's waves share).
-template <int D, int MT, int NL, bool BROWS>
+// MT full row tiles per first-group wave, MTB (0, 1 or MT) per second-group wave; NL
+// leftover tiles (0..2) per block, split over the first wave group by keys.  Block tiles
+// t0 .. t0 + 4 MT - 1 belong to the first group, the next 4 MTB to the second, then the
+// leftover tiles.  MTB < MT keeps padding rows off the SIMDs (with MTB = 0 the second group
+// only builds V^T).
+template <int D, int MT, int NL, int MTB>
 __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) {
   using Y = Layout<D>;
   constexpr int DS = D / 32;  // 32-wide d steps of the score product
@@ -175,6 +178,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   constexpr int DPW = Y::kDmaPerWave;
   constexpr int P = 2 * DPW;  // direct loads per first-group wave per tile (K and V)
   constexpr int MTA = MT > 0 ? MT : 1;
+  static_assert(MTB == 0 || MTB == 1 || MTB == MT, "second-group tiles: 0, 1 or MT");
   constexpr bool LEFT = NL > 0;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[Y::kBytes];
 
@@ -238,7 +242,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   // reads for its own rows, and the leftover scores are never computed twice.
   constexpr int LKB = NL == 2 ? 2 : 1;  // 16-key blocks per tile per wave
   const bool has_left = LEFT && wg == 0;
-  const int ltile = t0 + kWaves * MT + (NL == 2 ? (ww >> 1) : 0);
+  const int ltile = t0 + 4 * (MT + MTB) + (NL == 2 ? (ww >> 1) : 0);
   const int lh = NL == 2 ? (ww & 1) : (ww >> 1);  // the wave's leftover half
   const int ljj = NL == 2 ? 0 : (ww & 1);         // its first 16-key block in that half
   bf16x8 qopl[DS];
@@ -349,7 +353,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   // keys 32 h + 16 j + 4 grp + r in sc[.][j][r]; keys past the chunk end get -inf
   auto scores = [&](auto tag, int t, int h, f32x4 (&sc)[MTA][2], f32x4 (&scl)[2]) {
     constexpr bool WL = decltype(tag)::value;
-    constexpr int MTE = decltype(tag)::rows ? MT : 0;  // row tiles this wave computes
+    constexpr int MTE = decltype(tag)::rows;  // row tiles this wave computes
     __builtin_amdgcn_sched_barrier(0);
     const unsigned char* Ks = lds + ring_slot(Y::kKRing, t, kKStages);
     const int key0 = kbeg + t * kKeyTile;
@@ -426,7 +430,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   // always holds a valid key)
   auto set_reference = [&](auto tag) {
     constexpr bool WL = decltype(tag)::value;
-    constexpr int MTE = decltype(tag)::rows ? MT : 0;
+    constexpr int MTE = decltype(tag)::rows;
     f32x4 sc[MTA][2];
     f32x4 scl[2];
     scores(tag, 0, 0, sc, scl);
@@ -452,7 +456,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   // ---- softmax of the scores of half h (from scores()): probabilities, P^T operands
   auto softmax = [&](auto tag, int h, f32x4 (&sc)[MTA][2], f32x4 (&scl)[2]) {
     constexpr bool WL = decltype(tag)::value;
-    constexpr int MTE = decltype(tag)::rows ? MT : 0;
+    constexpr int MTE = decltype(tag)::rows;
     // ---- probabilities against the running reference (fp32), rounded to the fp16 P^T
     // operands; the row sums add exactly those rounded values (in fp32), so numerator and
     // normaliser weight every key alike.  ln: the running sum with this half's values.
@@ -551,7 +555,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   // ---- PV(t, h): O^T[d][row] += V^T[d][key] P^T[key][row] for keys 32 h .. 32 h + 31 of tile t
   auto pv = [&](auto tag, int t, int h) {
     constexpr bool WL = decltype(tag)::value;
-    constexpr int MTE = decltype(tag)::rows ? MT : 0;
+    constexpr int MTE = decltype(tag)::rows;
     __builtin_amdgcn_sched_barrier(0);
     const unsigned char* Vt = lds + ring_slot(Y::kVt, t, kVtStages) + vt_lane[h];
     f16x8 vop[DB];
@@ -610,7 +614,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   // VALU phase.
   auto run_chunk = [&](auto group) {
     constexpr bool LAG = decltype(group)::value;  // second wave group
-    constexpr PassTag<!LAG && LEFT, !LAG || BROWS> tag{};
+    constexpr PassTag<!LAG && LEFT, LAG ? MTB : MT> tag{};
     // Prologue: tiles 0 and 1 (the first iteration needs both) and the query operands, then
     // tile 2.  The compiler does not count direct loads, so it would wait for every one of
     // them (vmcnt(0)) before the first use of the query registers; an explicit full wait
@@ -618,7 +622,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     if constexpr (!LAG)
       for (int t = 0; t < 2 && t < ntiles; ++t) issue(t);
 #pragma unroll
-    for (int k = 0; k < MT; ++k) load_q(full_tile(k), qop[k]);
+    for (int k = 0; k < decltype(tag)::rows; ++k) load_q(full_tile(k), qop[k]);
     if constexpr (decltype(tag)::value) load_q(ltile, qopl);
     __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
     if constexpr (!LAG)
@@ -672,7 +676,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     for (int k = 0; k < MT; ++k) {
       const int tile = full_tile(k);
       const float lt = group_sum(l_run[k]);
-      if (tile >= t_end) continue;
+      if (tile >= t_end || (wg != 0 && k >= MTB)) continue;  // (no rows of this wave)
       const float inv = 1.f / lt;
       // chunk c of row r sits at chunk position c ^ r (conflict-free both ways)
 #pragma unroll
@@ -740,58 +744,63 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   }
 }
 
-template <int D, int MT, int NL, bool BROWS = true>
+template <int D, int MT, int NL, int MTB>
 hipError_t launch_cfg(const PrefixArgs& a, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((prefix_attn_splitk<D, MT, NL, BROWS>), grid, dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((prefix_attn_splitk<D, MT, NL, MTB>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, int MT>
-hipError_t launch_mt(const PrefixArgs& a, int nl, dim3 grid, hipStream_t stream) {
-  switch (nl) {
-    case 0: return launch_cfg<D, MT, 0>(a, grid, stream);
-    case 1: return launch_cfg<D, MT, 1>(a, grid, stream);
-    case 2: return launch_cfg<D, MT, 2>(a, grid, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
+// Row-tile shape of a block: MT tiles per first-group wave, MTB per second-group wave, NL
+// leftover tiles split by keys over the first group.
+struct RowShape {
+  int mt, nl, mtb;
+};
 
-// tiles_per_block <= 4 with one tile per wave: the first group holds every tile
+// The shapes the kernel is built for.  The register budget of two waves per SIMD (256 VGPRs,
+// no scratch) admits (MT, NL) in {(0..1, 0..2), (2, 0..1)} for the first group.  An idle
+// second group (MTB = 0) is kept to blocks of at most 4 tiles: with 5 or 6 tiles as one
+// tile per first-group wave plus leftover keys, the prefix pass alone timed the same as one
+// tile per wave of both groups, but whole steps on ragged batches (80 rows per KV head)
+// measured slower.
+constexpr RowShape kShapes[] = {
+    {0, 1, 0}, {0, 2, 0}, {1, 0, 0}, {1, 0, 1}, {1, 1, 1},
+    {1, 2, 1}, {2, 0, 1}, {2, 1, 1}, {2, 0, 2}, {2, 1, 2},
+};
+
 template <int D>
-hipError_t launch_d(const PrefixArgs& a, int mt, int nl, dim3 grid, hipStream_t stream) {
-  if (mt == 1 && nl == 0 && a.tiles_per_block <= kWaves / 2)
-    return launch_cfg<D, 1, 0, false>(a, grid, stream);
-  switch (mt) {
-    case 0: return launch_mt<D, 0>(a, nl, grid, stream);
-    case 1: return launch_mt<D, 1>(a, nl, grid, stream);
-    case 2: return launch_mt<D, 2>(a, nl, grid, stream);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_d(const PrefixArgs& a, RowShape r, dim3 grid, hipStream_t stream) {
+#define HTA_SHAPE(M, L, MB) \
+  if (r.mt == M && r.nl == L && r.mtb == MB) return launch_cfg<D, M, L, MB>(a, grid, stream);
+  HTA_SHAPE(0, 1, 0) HTA_SHAPE(0, 2, 0) HTA_SHAPE(1, 0, 0) HTA_SHAPE(1, 0, 1) HTA_SHAPE(1, 1, 1)
+  HTA_SHAPE(1, 2, 1) HTA_SHAPE(2, 0, 1) HTA_SHAPE(2, 1, 1) HTA_SHAPE(2, 0, 2) HTA_SHAPE(2, 1, 2)
+#undef HTA_SHAPE
+  return hipErrorInvalidValue;
 }
 
-// Tiles per workgroup: 8 * mt full tiles plus nl leftover tiles.  The register budget of
-// two waves per SIMD (256 VGPRs, no scratch) admits (mt, nl) in {(0..1, 0..2), (2, 0..1)}:
-// at most 17 tiles (272 query rows) per workgroup; more rows are split into row blocks.
-// Any other tile count rounds up to 8 * mt slots (the surplus slots compute nothing useful).
-void split_rows(int tiles, int* mt, int* nl) {
-  const int m = tiles / 8, r = tiles % 8;
-  if (r == 0 || (r == 1 && m <= 2) || (r == 2 && m <= 1)) {
-    *mt = m;
-    *nl = r;
-  } else {
-    *mt = (tiles + 7) / 8;
-    *nl = 0;
+// Matrix-core load of a shape on each SIMD (one wave of each group), in row tiles per key
+// tile: a leftover tile is spread over the four first-group waves.
+constexpr int simd_load4(RowShape r) { return 4 * (r.mt + r.mtb) + r.nl; }
+
+// The shape for `tiles` row tiles: the one that holds them all (4 (MT + MTB) + NL >= tiles)
+// with the least matrix-core work per SIMD.  Up to 17 tiles (272 query rows) fit one
+// workgroup; more rows are split into row blocks.
+RowShape split_rows(int tiles) {
+  RowShape best{2, 1, 2};
+  for (const RowShape& r : kShapes) {
+    if (4 * (r.mt + r.mtb) + r.nl < tiles) continue;
+    if (simd_load4(r) < simd_load4(best)) best = r;
   }
+  return best;
 }
 
 }  // namespace
 
-void prefix_row_blocking(const Geometry& g, int* mt, int* tiles_per_block, int* blocks) {
+void prefix_row_blocking(const Geometry& g, int* tiles_per_block, int* blocks) {
+  // The fewest blocks: each extra block streams the chunk's K and V once more, and a block
+  // with fewer tiles saves less than that (the per-tile staging and V^T work stays).
   const int max_tiles = 8 * 2 + 1;
   const int nb = (g.NT + max_tiles - 1) / max_tiles;
   const int tpb = (g.NT + nb - 1) / nb;
-  int nl;
-  split_rows(tpb, mt, &nl);
   *blocks = (g.NT + tpb - 1) / tpb;
   *tiles_per_block = tpb;
 }
@@ -808,15 +817,15 @@ hipError_t launch_prefix_attn_splitk(const Geometry& g, const void* q, const voi
   a.lse_part = ws.lse_part;
   a.o_part = ws.o_part;
   a.g = g;
-  int mt, tpb, nb, nl;
-  prefix_row_blocking(g, &mt, &tpb, &nb);
-  split_rows(tpb, &mt, &nl);
+  int tpb, nb;
+  prefix_row_blocking(g, &tpb, &nb);
+  const RowShape shape = split_rows(tpb);
   a.row_blocks = nb;
   a.tiles_per_block = tpb;
   a.c = g.scale * kLog2e;
   dim3 grid(g.S, g.Hkv * nb, g.B);
-  if (g.D == 128) return launch_d<128>(a, mt, nl, grid, stream);
-  if (g.D == 64) return launch_d<64>(a, mt, nl, grid, stream);
+  if (g.D == 128) return launch_d<128>(a, shape, grid, stream);
+  if (g.D == 64) return launch_d<64>(a, shape, grid, stream);
   return hipErrorInvalidValue;
 }
 
