@@ -105,16 +105,18 @@ typedef struct {
 /* How a descriptor is executed; filled by hta_plan().  Sizes in bytes, offsets into the
  * workspace.  Partial results of split s (s < num_splits: prefix keys
  * [s*chunk, min((s+1)*chunk, prefix_len[b])); s == num_splits: the tree keys) live at
- *   lse_part[((b*Hkv + g)*(num_splits+1) + s)*rows_padded + r]              (float)
- *   o_part row (((b*Hkv + g)*(num_splits+1) + s)*rows_padded + r)          (3*D bytes)
- * where row r = i*(Hq/Hkv) + (h % (Hq/Hkv)) packs the query heads sharing KV head g.
- * o_part holds the normalised partial output, lse_part its natural-log normaliser
- * (-inf for an empty chunk).  Splits at or past ceil(prefix_len[b]/chunk) are not written.
- * An o_part row stores each value as the top 24 bits of its fp32 bit pattern (rounded to
- * nearest even at bit 8; relative error at most 2^-16), values 4j..4j+3 in the three
- * little-endian uint32 words 3j..3j+2 of the row:
- *   w0 = x0[31:8] | x1[15:8] << 24,  w1 = x1[31:16] | x2[23:8] << 16,
- *   w2 = x2[31:24] | x3[31:8] << 8   (x = the rounded fp32 bit patterns). */
+ *   lse_part[n], o_scale[n]                                                  (float)
+ *   o_part row n                                                             (2*D bytes)
+ * with n = ((b*Hkv + g)*(num_splits+1) + s)*rows_padded + r, where row r =
+ * i*(Hq/Hkv) + (h % (Hq/Hkv)) packs the query heads sharing KV head g.  o_part holds the
+ * normalised partial output, lse_part its natural-log normaliser (-inf for an empty chunk).
+ * Splits at or past ceil(prefix_len[b]/chunk) are not written.
+ * An o_part row stores D little-endian int16 values q_d (q_0 first); value d of the row is
+ * q_d * o_scale[n].  The writer takes m >= max_d |x_d| (the row's largest magnitude, or a
+ * bound on it no larger than the largest |v| the row attends to) and sets o_scale = m / 32767
+ * and q_d = x_d * 32767 / m rounded to the nearest integer (ties to even), so |q_d| <= 32767
+ * and a value's error is at most 2^-16 m (plus fp32 rounding); o_scale is 0 for an all-zero
+ * row and NaN for a row holding a non-finite value. */
 typedef struct {
     int32_t chunk;          /* prefix keys per split */
     int32_t num_splits;     /* ceil(max_prefix_len / chunk), at least 1 */
@@ -124,6 +126,7 @@ typedef struct {
     size_t masks_offset;    /* uint64 [B, T, ceil(T/64)] */
     size_t lse_part_offset;
     size_t o_part_offset;
+    size_t o_scale_offset;  /* float, one per o_part row */
     size_t workspace_bytes; /* total, == hta_workspace_size() */
 } hta_plan_info;
 

@@ -65,42 +65,41 @@ def test_plan_llama_shape():
     assert p.workspace_bytes == hta.workspace_size(_desc())
     # partial buffers hold (splits + 1) slots: the last one is the tree partial
     n = 8 * (p.num_splits + 1) * 272
-    assert p.o_part_offset >= p.lse_part_offset + 4 * n
-    # o_part rows: 128 values packed to 24 bits each
-    assert p.workspace_bytes >= p.o_part_offset + 3 * n * 128
+    assert p.o_scale_offset >= p.lse_part_offset + 4 * n
+    assert p.o_part_offset >= p.o_scale_offset + 4 * n
+    # o_part rows: 128 int16 values each
+    assert p.workspace_bytes >= p.o_part_offset + 2 * n * 128
 
 
-def _round24(bits: np.ndarray) -> np.ndarray:
-    """fp32 bit patterns rounded to their top 24 bits, nearest even (include/hta.h)."""
-    b = bits.astype(np.uint64)
-    r = (b + 0x7F + ((b >> 8) & 1)) & 0xFFFFFF00
-    return (r & 0xFFFFFFFF).astype(np.uint32)
-
-
-def test_partial_views_decode_the_documented_packing():
-    """The packed o_part layout written out from its description in include/hta.h (an
-    encoder of its own) and read back through partial_views, on the CPU."""
+def test_partial_views_decode_the_documented_encoding():
+    """The o_part rows and their factors written out from their description in include/hta.h
+    (an encoder of its own) and read back through partial_views, on the CPU."""
     d = _desc(batch=1, num_q_heads=4, num_kv_heads=4, head_dim=64, tree_size=3,
               max_prefix_len=256)
     p = hta.plan(d)
     n = 1 * 4 * (p.num_splits + 1) * p.rows_padded
     rng = np.random.default_rng(5)
-    vals = (rng.standard_normal((n, 64)) * np.exp2(rng.integers(-20, 20, (n, 64)))).astype(np.float32)
-    vals[0, :4] = [0.0, -0.0, 1.0 + 2.0 ** -16, 1.0 + 3 * 2.0 ** -16]  # ties round to even
-    x = _round24(vals.view(np.uint32)).reshape(n, 16, 4)
-    x0, x1, x2, x3 = (x[..., i] for i in range(4))
-    w0 = (x0 >> 8) | ((x1 >> 8) & 0xFF) << 24
-    w1 = (x1 >> 16) | ((x2 >> 8) & 0xFFFF) << 16
-    w2 = (x2 >> 24) | (x3 >> 8) << 8
-    words = np.stack((w0, w1, w2), axis=-1).astype(np.uint32)
+    vals = (rng.standard_normal((n, 64)) * np.exp2(rng.integers(-20, 20, (n, 1)))).astype(np.float32)
+    vals[1] = 0.0                                       # an all-zero row: factor 0
+    vals[2] = np.linspace(-1.0, 1.0, 64, dtype=np.float32)
+    vals[2, :3] = [-3.0, 1.5, 0.75]                     # -3 is the largest magnitude
+    m = np.max(np.abs(vals), axis=1)
+    scale = (m / np.float32(32767)).astype(np.float32)
+    enc = np.where(m > 0, np.float32(32767) / np.where(m > 0, m, 1), 0).astype(np.float32)
+    q = np.rint(vals * enc[:, None]).astype(np.int16)   # nearest, ties to even
+    assert q[2, 0] == -32767 and np.abs(q).max() == 32767
     ws = torch.zeros(p.workspace_bytes, dtype=torch.uint8)
-    ws[p.o_part_offset:p.o_part_offset + 3 * n * 64] = torch.from_numpy(words.view(np.uint8).reshape(-1))
+    ws[p.o_scale_offset:p.o_scale_offset + 4 * n] = torch.from_numpy(scale.view(np.uint8))
+    ws[p.o_part_offset:p.o_part_offset + 2 * n * 64] = torch.from_numpy(
+        q.reshape(-1).view(np.uint8))
     _, o = hta.partial_views(d, ws)
     got = o.reshape(n, 64).numpy()
-    want = x.reshape(n, 64).view(np.float32)
-    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
-    assert got[0, 2] == 1.0 and got[0, 3] == 1.0 + 2.0 ** -14  # nearest even
-    assert np.max(np.abs(got - vals) / np.maximum(np.abs(vals), 1e-30)) <= 2.0 ** -16
+    assert np.array_equal(got, q.astype(np.float32) * scale[:, None])
+    assert not got[1].any()
+    # the documented bound: 2^-16 of the row's largest magnitude, plus fp32 rounding (of the
+    # factors and of the products: a few 2^-24 of the magnitude, i.e. under 1% of the bound)
+    err = np.abs(got.astype(np.float64) - vals) / np.maximum(m, 1e-30)[:, None]
+    assert err.max() <= 2.0 ** -16 * 1.01
 
 
 @pytest.mark.parametrize("kw,code", [

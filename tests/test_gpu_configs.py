@@ -42,5 +42,5 @@ def test_tiny_fp32_config():
     assert w.dtype == torch.float32
     _log(f"config {w.name}")
     out, lse = run_gpu(w)
-    # fp32 arithmetic; outputs also carry the 24-bit storage of the split-K partials
+    # fp32 arithmetic; outputs also carry the 16-bit storage of the split-K partials
     check_rows(w, out, lse, out_tol=1e-4, lse_tol=2e-5)

@@ -422,8 +422,10 @@ def test_prefix_len_out_of_range_is_flagged():
 # ----------------------------------------------------------------------------- fp32 inputs
 
 F32_TOL = 2e-5  # exact fp32 arithmetic against the fp64 oracle (log-sum-exp)
-# outputs: the split-K partials pass through memory as 24-bit floats (relative error at most
-# 2^-16, include/hta.h), so |out - oracle| <= 2^-16 max|v| + fp32 rounding; max|v| < 6 here
+# outputs: the split-K partials pass through memory as 16-bit values with one factor per row
+# (error at most 2^-16 of the row's largest magnitude, include/hta.h); a partial row is a
+# convex combination of V rows, so |out - oracle| <= 2^-16 max|v| + fp32 rounding; max|v| < 6
+# here
 F32_OUT_TOL = 1e-4
 
 

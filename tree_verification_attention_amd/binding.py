@@ -86,6 +86,7 @@ class hta_plan_info(ctypes.Structure):
         ("masks_offset", ctypes.c_size_t),
         ("lse_part_offset", ctypes.c_size_t),
         ("o_part_offset", ctypes.c_size_t),
+        ("o_scale_offset", ctypes.c_size_t),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -671,20 +672,15 @@ def accept_commit(logits, tokens, root_token, parent_idx, prefix_len, k_prefix, 
 
 def partial_views(desc: hta_desc, workspace: torch.Tensor):
     """(lse_part [B,Hkv,S+1,R_pad] view, o_part [B,Hkv,S+1,R_pad,D] decoded fp32 copy) of a
-    workspace.  o_part rows are stored as packed 24-bit values (include/hta.h); this decodes
-    them with torch integer ops on the workspace's device (inspection and tests only)."""
+    workspace.  o_part rows are stored as int16 values with one fp32 factor per row
+    (include/hta.h); this decodes them with torch ops on the workspace's device (inspection
+    and tests only)."""
     p = plan(desc)
     B, Hkv, D = desc.batch, desc.num_kv_heads, desc.head_dim
     S1, Rp = p.num_splits + 1, p.rows_padded
     n = B * Hkv * S1 * Rp
     lse = workspace[p.lse_part_offset:p.lse_part_offset + 4 * n].view(torch.float32)
-    raw = workspace[p.o_part_offset:p.o_part_offset + 3 * n * D].view(torch.int32)
-    w = raw.view(n, D // 4, 3)
-    w0, w1, w2 = w[..., 0], w[..., 1], w[..., 2]
-    low = -256  # 0xFFFFFF00 as int32
-    x0 = w0 << 8
-    x1 = (((w0 >> 16) & 0xFFFF) | (w1 << 16)) & low
-    x2 = (((w1 >> 8) & 0xFFFFFF) | (w2 << 24)) & low
-    x3 = w2 & low
-    o = torch.stack((x0, x1, x2, x3), dim=-1).view(torch.float32)
+    scale = workspace[p.o_scale_offset:p.o_scale_offset + 4 * n].view(torch.float32)
+    q = workspace[p.o_part_offset:p.o_part_offset + 2 * n * D].view(torch.int16)
+    o = q.view(n, D).to(torch.float32) * scale.view(n, 1)
     return lse.view(B, Hkv, S1, Rp), o.reshape(B, Hkv, S1, Rp, D)

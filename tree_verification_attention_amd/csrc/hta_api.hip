@@ -89,8 +89,10 @@ hta_status make_plan(const hta_desc* d, Geometry* g, hta_plan_info* info) {
   const size_t parts = (size_t)G.B * G.Hkv * (size_t)(G.S + 1) * G.R_pad;
   p.lse_part_offset = off;
   off = round_up(off + sizeof(float) * parts, 256);
+  p.o_scale_offset = off;
+  off = round_up(off + sizeof(float) * parts, 256);
   p.o_part_offset = off;
-  off = round_up(off + 3 * parts * G.D, 256);  // packed 24-bit values
+  off = round_up(off + 2 * parts * G.D, 256);  // 16-bit values
   p.workspace_bytes = off;
   if (g) *g = G;
   if (info) *info = p;
@@ -103,6 +105,7 @@ Workspace carve(void* base, const hta_plan_info& p) {
   w.status = (int32_t*)(c + p.status_offset);
   w.masks = (uint64_t*)(c + p.masks_offset);
   w.lse_part = (float*)(c + p.lse_part_offset);
+  w.o_scale = (float*)(c + p.o_scale_offset);
   w.o_part = (uint32_t*)(c + p.o_part_offset);
   w.status_reset = nullptr;
   return w;

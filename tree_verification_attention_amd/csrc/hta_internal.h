@@ -45,56 +45,45 @@ struct Workspace {
   int32_t* status;      // [B]
   uint64_t* masks;      // [B, T, W]
   float* lse_part;      // [B, Hkv, S+1, R_pad]
-  uint32_t* o_part;     // [B, Hkv, S+1, R_pad, D] packed 24-bit values: 3 D / 4 dwords a row
+  float* o_scale;       // [B, Hkv, S+1, R_pad]: the factor of each o_part row
+  uint32_t* o_part;     // [B, Hkv, S+1, R_pad, D] 16-bit fixed point: D / 2 dwords a row
   // When set (== status), the prefix pass clears the status words first: a call whose later
   // launch records bits with atomic ORs starts from zero.  nullptr leaves them alone.
   int32_t* status_reset;
 };
 
-// Split-K partial outputs travel through memory as packed 24-bit floats: the top 24 bits of
-// the fp32 value (sign, 8-bit exponent, 15 mantissa bits), rounded to nearest even, four
-// values in three dwords.  The relative error is at most 2^-16 (normalised partials are
-// bounded by max |v|), and the partial traffic -- written by the prefix pass, read by the
-// merge -- is three quarters of fp32.
-struct Packed24 {
-  uint32_t w[3];
+// Split-K partial output rows travel through memory as 16-bit fixed point with one fp32
+// factor per row: value d of a row is q_d * f, where f = m / 32767 for the row's largest
+// magnitude m (or a bound on it, at most the largest |v| the row attends to) and q_d is
+// x_d / f rounded to the nearest integer (ties to even), |q_d| <= 32767.  A value's error is
+// at most f / 2 = 2^-16 m (plus fp32 rounding): since a partial row is a convex combination
+// of V rows, the merged output's error from this storage is at most 2^-16 max |v|.  The
+// partial traffic -- written by the prefix pass, read by the merge -- is half of fp32.  An
+// all-zero row has f = 0; a row holding a non-finite value gets f = NaN, so the merge's
+// result is non-finite.  Two values per dword: value 2j in the low half of word j.
+struct RowCode {
+  float f;    // the stored factor
+  float enc;  // 1 / f (0 for an all-zero row)
 };
-__device__ __forceinline__ uint32_t round24(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7Fu + ((u >> 8) & 1u)) & 0xFFFFFF00u;
+// amax: max |x| over the row (or the bound m); sum: the sum of the row's values (non-finite
+// iff one of them is)
+__device__ __forceinline__ RowCode row_code(float amax, float sum) {
+  RowCode c;
+  const bool finite = __builtin_isfinite(sum);
+  c.f = finite ? amax * (1.f / 32767.f) : __builtin_nanf("");
+  c.enc = (finite && amax > 0.f) ? 32767.f / amax : 0.f;
+  return c;
 }
-__device__ __forceinline__ Packed24 pack24(f32x4 v) {
-  const uint32_t r0 = round24(v[0]), r1 = round24(v[1]), r2 = round24(v[2]), r3 = round24(v[3]);
-  Packed24 p;
-  p.w[0] = (r0 >> 8) | (r1 << 16);
-  p.w[1] = (r1 >> 16) | (r2 << 8);
-  p.w[2] = (r2 >> 24) | r3;
-  return p;
+__device__ __forceinline__ uint32_t pack16(float x0, float x1, float enc) {
+  const int q0 = (int)__builtin_rintf(x0 * enc), q1 = (int)__builtin_rintf(x1 * enc);
+  return ((uint32_t)q0 & 0xFFFFu) | ((uint32_t)q1 << 16);
 }
-__device__ __forceinline__ f32x4 unpack24(Packed24 p) {
-  f32x4 v;
-  v[0] = __uint_as_float(p.w[0] << 8);
-  v[1] = __uint_as_float(((p.w[0] >> 16) | (p.w[1] << 16)) & 0xFFFFFF00u);
-  v[2] = __uint_as_float(((p.w[1] >> 8) | (p.w[2] << 24)) & 0xFFFFFF00u);
-  v[3] = __uint_as_float(p.w[2] & 0xFFFFFF00u);
-  return v;
+// four values (one f32x4) -> two dwords
+__device__ __forceinline__ uint2 pack16x4(f32x4 v, float enc) {
+  return make_uint2(pack16(v[0], v[1], enc), pack16(v[2], v[3], enc));
 }
-// Store / load group g (values 4 g .. 4 g + 3) of a packed row.
-__device__ __forceinline__ void store24(uint32_t* row, int g, f32x4 v) {
-  const Packed24 p = pack24(v);
-  uint32_t* d = row + 3 * g;
-  d[0] = p.w[0];
-  d[1] = p.w[1];
-  d[2] = p.w[2];
-}
-__device__ __forceinline__ f32x4 load24(const uint32_t* row, int g) {
-  const uint32_t* s = row + 3 * g;
-  Packed24 p;
-  p.w[0] = s[0];
-  p.w[1] = s[1];
-  p.w[2] = s[2];
-  return unpack24(p);
-}
+__device__ __forceinline__ float lo16(uint32_t w) { return (float)(int)(short)(w & 0xFFFFu); }
+__device__ __forceinline__ float hi16(uint32_t w) { return (float)((int)w >> 16); }
 
 // Host launchers (each enqueues exactly one kernel on the stream).
 hipError_t launch_prefix_attn_splitk(const Geometry& g, const void* q, const void* k_prefix,

@@ -12,7 +12,8 @@
 //
 // One wave per output row (b, i, h), in four part groups of 16 lanes: group g handles prefix
 // splits g, g+4, g+8, ... and each of its lanes owns D/16 consecutive output dimensions
-// (16- or 32-byte loads), so a group reads whole 512-byte partial rows.  Every load of the
+// (8- or 16-byte loads of the 16-bit partial values), so a group reads whole partial rows;
+// the row's factor (o_scale) and log-sum-exp come with them.  Every load of the
 // first 36 splits (their log-sum-exps and partial rows), the tree part and the sequence's
 // prefix length is issued before any is used, so the merge costs one memory round trip: the
 // slots of splits past the prefix end are read speculatively and never used (they
@@ -51,7 +52,8 @@ struct MergeArgs {
                            // are OR-ed in (the call cleared the words first, or the tree pass
                            // wrote them)
   float* lse_part;               // read by the merges, written by the tree-only form
-  uint32_t* o_part;              // packed 24-bit rows (load24 / store24)
+  float* o_scale;                // the factor of each o_part row (likewise)
+  uint32_t* o_part;              // 16-bit rows (pack16 / lo16, hi16)
   float* out;
   float* lse;
   // fused merge only
@@ -86,12 +88,24 @@ __device__ inline float to_f32(float x) { return x; }
 // tree part fused in, or the tree part alone written as the tree partial (slot S).
 enum Mode { kPlain = 0, kFused = 1, kTreeOnly = 2 };
 
-// sum over the 16 lanes of a part group
+// sum and maximum over the 16 lanes of a part group
 __device__ inline float lane16_sum(float x) {
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o);
   return x;
 }
+__device__ inline float lane16_max(float x) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// One lane's share of a partial row: NW dwords of 16-bit values (two per dword), loaded
+// whole (16 bytes at D = 128, 8 at D = 64).
+template <int NW>
+struct Share16 {
+  uint32_t w[NW];
+};
 
 // maximum over the four part groups (lanes l, l^16, l^32, l^48)
 __device__ inline float group_max4(float x) {
@@ -107,7 +121,8 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   constexpr bool FUSED = MODE != kPlain;   // computes the tree part
   constexpr bool PREFIX = MODE != kTreeOnly;
   constexpr int DPL = D / 16;   // output dimensions per lane of a part group
-  constexpr int NV = DPL / 4;   // packed 4-value groups per part and lane
+  constexpr int NW = DPL / 2;   // dwords of 16-bit values per part and lane
+  using Sh = Share16<NW>;
   constexpr int kBatch = 9;     // splits per lane per pass: 36 per pass
   __shared__ int32_t s_par[kThreads / 64][kMaxT];  // fused: parent pointers, one slice per wave
   const Geometry& G = a.g;
@@ -127,15 +142,21 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   float* lsep = a.lse + ((size_t)b * G.Hq + h) * T + i;
   const size_t base = ((size_t)b * G.Hkv + kv) * (G.S + 1);
   const float* lrow = a.lse_part + base * G.R_pad + r;                 // slot s at s * R_pad
-  // packed partial row of slot 0 (slot s at s * ostride); this lane's groups NV dl + j
-  const uint32_t* orow = a.o_part + (base * G.R_pad + r) * (3 * D / 4);
-  const size_t ostride = (size_t)G.R_pad * (3 * D / 4);
-  auto load_groups = [&](int slot_s, Packed24 (&dst)[NV]) {
-    const uint32_t* src = orow + (size_t)slot_s * ostride + 3 * NV * dl;
-#pragma unroll
-    for (int j = 0; j < NV; ++j)
-#pragma unroll
-      for (int w = 0; w < 3; ++w) dst[j].w[w] = src[3 * j + w];
+  const float* frow = a.o_scale + base * G.R_pad + r;                  // (likewise)
+  // partial row of slot 0 (slot s at s * ostride); this lane's dwords NW dl ..
+  const uint32_t* orow = a.o_part + (base * G.R_pad + r) * (D / 2);
+  const size_t ostride = (size_t)G.R_pad * (D / 2);
+  auto load_share = [&](int slot_s) {
+    const uint32_t* src = orow + (size_t)slot_s * ostride + NW * dl;
+    Sh v;
+    if constexpr (NW == 4) {
+      const uint4 x = *(const uint4*)src;
+      v.w[0] = x.x, v.w[1] = x.y, v.w[2] = x.z, v.w[3] = x.w;
+    } else {
+      const uint2 x = *(const uint2*)src;
+      v.w[0] = x.x, v.w[1] = x.y;
+    }
+    return v;
   };
   const bool tree_slot = MODE == kPlain && a.include_tree;  // the plain merge's tree partial
 
@@ -147,14 +168,10 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   // branch, which would serialise the loads instead of having them all in flight.
   const float lse_raw = PREFIX ? lrow[(size_t)min(lane, G.S - 1) * G.R_pad] : 0.f;
   const float lse_lane = (PREFIX && lane < G.S) ? lse_raw : -INFINITY;
-  Packed24 vt[NV];  // the plain merge's tree partial (slot S, always allocated)
+  Sh vt = {};  // the plain merge's tree partial (slot S, always allocated) and its factor
   const float lse_tree_raw = FUSED ? 0.f : lrow[(size_t)G.S * G.R_pad];
-  if constexpr (FUSED) {
-#pragma unroll
-    for (int j = 0; j < NV; ++j) vt[j] = Packed24{{0u, 0u, 0u}};
-  } else {
-    load_groups(G.S, vt);
-  }
+  const float f_tree = FUSED ? 0.f : frow[(size_t)G.S * G.R_pad];
+  if constexpr (!FUSED) vt = load_share(G.S);
   const float lse_tree = tree_slot ? lse_tree_raw : -INFINITY;
   int par[kMaxT / 64];
   float qv[DPL];
@@ -169,19 +186,20 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) qv[e] = to_f32(qp[e]);
   }
-  float lk[kBatch];
-  Packed24 v[kBatch][NV];
+  float lk[kBatch], fk[kBatch];
+  Sh v[kBatch];
   auto load_parts = [&](int k0, int k1) {
 #pragma unroll
     for (int k = k0; k < k1; ++k) {
       // slot pg + 4k, clamped: lanes past the last split re-read it and never use it
       const int p = min(pg + 4 * k, G.S - 1);
       lk[k] = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < NV; ++j) v[k][j] = Packed24{{0u, 0u, 0u}};
+      fk[k] = 0.f;
+      v[k] = Sh{};
       if (PREFIX && 4 * k < G.S) {  // wave-uniform
         lk[k] = lrow[(size_t)p * G.R_pad];
-        load_groups(p, v[k]);
+        fk[k] = frow[(size_t)p * G.R_pad];
+        v[k] = load_share(p);
       }
     }
   };
@@ -289,19 +307,27 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   }
 
   if constexpr (MODE == kTreeOnly) {  // normalise and write the tree partial (slot S)
-    // (the tree partial of a rejected tree is NaN)
+    // (16-bit values with the row's factor from a 16-lane reduction; the tree partial of a
+    // rejected tree has a NaN factor and log-sum-exp)
     const float ltot = group_sum4(lt);
     const float inv = 1.f / ltot;
-    uint32_t* trow = a.o_part + ((base + G.S) * G.R_pad + r) * (3 * D / 4);
+    float o[DPL], amax = 0.f, sum = 0.f;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      f32x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = bad ? NAN : group_sum4(at[4 * j + e]) * inv;
-      if (pg == 0) store24(trow, NV * dl + j, o);
+    for (int e = 0; e < DPL; ++e) {
+      o[e] = group_sum4(at[e]) * inv;
+      amax = fmaxf(amax, __builtin_fabsf(o[e]));
+      sum += o[e];
     }
-    if (lane == 0)
-      a.lse_part[(base + G.S) * G.R_pad + r] = bad ? NAN : (mt + __log2f(ltot)) * kLn2;
+    const RowCode rc = row_code(lane16_max(amax), lane16_sum(sum));
+    const size_t n = (base + G.S) * G.R_pad + r;
+    uint32_t* trow = a.o_part + n * (D / 2) + NW * dl;
+    if (pg == 0)
+#pragma unroll
+      for (int j = 0; j < NW; ++j) trow[j] = pack16(o[2 * j], o[2 * j + 1], rc.enc);
+    if (lane == 0) {
+      a.lse_part[n] = bad ? NAN : (mt + __log2f(ltot)) * kLn2;
+      a.o_scale[n] = bad ? NAN : rc.f;
+    }
     return;
   }
   if (bad) {  // a rejected sequence: NaN
@@ -344,26 +370,27 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
     const bool use_tree = tree_slot && pg == 0;
     const float wt = use_tree ? __builtin_amdgcn_exp2f((lse_tree - Mn) * kLog2e) : 0.f;
     wl += wt;
+    const float wf = wt * f_tree;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const f32x4 t = unpack24(vt[j]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[4 * j + e] = use_tree ? wt * t[e] : 0.f;
+    for (int j = 0; j < NW; ++j) {
+      acc[2 * j] = use_tree ? wf * lo16(vt.w[j]) : 0.f;
+      acc[2 * j + 1] = use_tree ? wf * hi16(vt.w[j]) : 0.f;
     }
   }
-  auto add_part = [&](float l, const Packed24 (&pv)[NV]) {
+  // (a part's weight times its row factor scales the 16-bit values directly)
+  auto add_part = [&](float l, float f, const Sh& pv) {
     const float w = __builtin_amdgcn_exp2f((l - Mn) * kLog2e);
     wl += w;
+    const float wf = w * f;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const f32x4 t = unpack24(pv[j]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[4 * j + e] += w * t[e];
+    for (int j = 0; j < NW; ++j) {
+      acc[2 * j] += wf * lo16(pv.w[j]);
+      acc[2 * j + 1] += wf * hi16(pv.w[j]);
     }
   };
 #pragma unroll
   for (int k = 0; k < kBatch; ++k)
-    if (pg + 4 * k < nsplit) add_part(lk[k], v[k]);
+    if (pg + 4 * k < nsplit) add_part(lk[k], fk[k], v[k]);
   // splits beyond the first 36 (long prefixes with many splits)
   for (int p0 = 4 * kBatch + pg; p0 < nsplit; p0 += 4 * kBatch) {
 #pragma unroll
@@ -371,12 +398,13 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
       const int p = p0 + 4 * k;
       if (p < nsplit) {
         lk[k] = lrow[(size_t)p * G.R_pad];
-        load_groups(p, v[k]);
+        fk[k] = frow[(size_t)p * G.R_pad];
+        v[k] = load_share(p);
       }
     }
 #pragma unroll
     for (int k = 0; k < kBatch; ++k)
-      if (p0 + 4 * k < nsplit) add_part(lk[k], v[k]);
+      if (p0 + 4 * k < nsplit) add_part(lk[k], fk[k], v[k]);
   }
   float wsum = group_sum4(wl);
 #pragma unroll
@@ -399,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   const bool row_bad = __builtin_amdgcn_ballot_w64(!finite) != 0;
   if (pg == 0) {
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
+    for (int j = 0; j < DPL / 4; ++j)
       ((float4*)outp)[j] = row_bad ? make_float4(NAN, NAN, NAN, NAN)
                                    : make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2],
                                                  acc[4 * j + 3]);
@@ -432,6 +460,7 @@ hipError_t launch_tree_mode(const Geometry& g, const void* q, const void* k_tree
   MergeArgs a = {};
   a.prefix_len = prefix_len;
   a.lse_part = ws.lse_part;
+  a.o_scale = ws.o_scale;
   a.o_part = ws.o_part;
   a.out = out;
   a.lse = lse;
@@ -455,6 +484,7 @@ hipError_t launch_lse_merge(const Geometry& g, const int32_t* prefix_len, bool i
   a.status = ws.status;  // read always, used only with the tree partial
   a.status_or = ws.status;
   a.lse_part = ws.lse_part;
+  a.o_scale = ws.o_scale;
   a.o_part = ws.o_part;
   a.out = out;
   a.lse = lse;

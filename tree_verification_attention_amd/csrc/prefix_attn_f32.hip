@@ -27,7 +27,8 @@ struct PrefixF32Args {
   const int32_t* prefix_len;
   int32_t* status_reset;  // [B] or nullptr: cleared by the first workgroup of b
   float* lse_part;
-  uint32_t* o_part;  // packed 24-bit rows (store24)
+  float* o_scale;    // the factor of each o_part row
+  uint32_t* o_part;  // 16-bit rows (pack16)
   Geometry g;
 };
 
@@ -99,15 +100,26 @@ __global__ __launch_bounds__(64 * kWaves) void prefix_attn_f32(PrefixF32Args a) 
       }
     }
     const float inv = 1.f / l;
-    // lane owns dims lane + 64 e; every fourth lane packs its group of four
-    uint32_t* orow = a.o_part + (slot * G.R_pad + r) * (3 * D / 4);
+    // lane owns dims lane + 64 e: the row's factor from a wave reduction, then every
+    // second lane packs its pair of values
+    float amax = 0.f, sum = 0.f;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
-      const float x = acc[e] * inv;
-      const f32x4 g4 = {x, __shfl_down(x, 1), __shfl_down(x, 2), __shfl_down(x, 3)};
-      if ((lane & 3) == 0) store24(orow, (lane + 64 * e) / 4, g4);
+      acc[e] *= inv;
+      amax = fmaxf(amax, __builtin_fabsf(acc[e]));
+      sum += acc[e];
     }
-    if (lane == 0) a.lse_part[slot * G.R_pad + r] = (m + __log2f(l)) * kLn2;
+    const RowCode rc = row_code(wave_max(amax), wave_sum(sum));
+    uint32_t* orow = a.o_part + (slot * G.R_pad + r) * (D / 2);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      const float x1 = __shfl_down(acc[e], 1);
+      if ((lane & 1) == 0) orow[(lane + 64 * e) / 2] = pack16(acc[e], x1, rc.enc);
+    }
+    if (lane == 0) {
+      a.lse_part[slot * G.R_pad + r] = (m + __log2f(l)) * kLn2;
+      a.o_scale[slot * G.R_pad + r] = rc.f;
+    }
     __builtin_amdgcn_wave_barrier();  // s_q is rewritten for the next row
   }
 }
@@ -124,6 +136,7 @@ hipError_t launch_prefix_attn_f32(const Geometry& g, const void* q, const void* 
   a.prefix_len = prefix_len;
   a.status_reset = ws.status_reset;
   a.lse_part = ws.lse_part;
+  a.o_scale = ws.o_scale;
   a.o_part = ws.o_part;
   a.g = g;
   dim3 grid(g.S, g.Hkv, g.B);

@@ -135,12 +135,13 @@ __device__ __forceinline__ void wait_and_barrier() {
 // access on CDNA3/CDNA4); bytes past num_records are dropped, never written.
 constexpr int kBufWord3 = 0x00020000;
 constexpr int kAgentScope = 16;  // the sc1 cache-policy bit
-typedef __attribute__((ext_vector_type(3))) unsigned u32x3;
-__device__ __forceinline__ void store24_agent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
-                                              f32x4 v) {
-  const Packed24 p = pack24(v);
-  __builtin_amdgcn_raw_buffer_store_b96(u32x3{p.w[0], p.w[1], p.w[2]}, r, byte_off, 0,
-                                        kAgentScope);
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+__device__ __forceinline__ void store_agent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, byte_off, 0, kAgentScope);
+}
+__device__ __forceinline__ void store_agent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, byte_off, 0, kAgentScope);
 }
 
 struct PrefixArgs {
@@ -150,7 +151,8 @@ struct PrefixArgs {
   const int32_t* prefix_len;       // [B]
   int32_t* status_reset;           // [B] or nullptr: cleared by the first workgroup of b
   float* lse_part;
-  uint32_t* o_part;                // packed 24-bit rows (store24)
+  float* o_scale;                  // the factor of each o_part row
+  uint32_t* o_part;                // 16-bit rows (pack16x4)
   Geometry g;
   int32_t row_blocks;              // query-row blocks per (b, kv head)
   int32_t tiles_per_block;         // row tiles per block
@@ -657,55 +659,86 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   if (wg == 0) run_chunk(std::false_type{});
   else run_chunk(std::true_type{});
 
-  // ---- normalise and write this chunk's partial
+  // ---- normalise and write this chunk's partial (16-bit rows with one factor per row)
   const size_t slot = ((size_t)b * G.Hkv + kv) * (G.S + 1) + s;
+  constexpr int kRowBytes = 2 * D;  // an encoded partial row
   const __amdgpu_buffer_rsrc_t part_rows = __builtin_amdgcn_make_buffer_rsrc(
-      a.o_part + slot * G.R_pad * (3 * D / 4), 0, G.R_pad * 3 * D, kBufWord3);
-  // A lane holds 4 consecutive dims of one row per d block, so direct stores would write
-  // small pieces of 16 rows per instruction.  Each wave stages its normalised rows in LDS
-  // (the V and V^T rings are free once every wave is past its loop) and writes them back
-  // whole, packed to 24 bits: every store instruction covers consecutive rows (two at
-  // D = 128, 768 bytes).
+      a.o_part + slot * G.R_pad * (D / 2), 0, G.R_pad * kRowBytes, kBufWord3);
+  float* lse_rows = a.lse_part + slot * G.R_pad;
+  float* scale_rows = a.o_scale + slot * G.R_pad;
+  // A row's factor is its largest magnitude over the 4 lanes that hold it (row_code).  A lane
+  // holds 4 consecutive dims of one row per d block, so direct stores would write 8-byte
+  // pieces of 16 rows per instruction: each wave stages its encoded rows in LDS (the V and
+  // V^T rings are free once every wave is past its loop) and writes them back whole, four
+  // consecutive rows (1 KB) per store instruction at D = 128.
   __syncthreads();
   {
-    constexpr int kC = D / 4;                        // 16-byte chunks per fp32 row
-    constexpr int kRowsPerInst = 64 * 16 / (D * 4);  // rows per store instruction
-    static_assert(Y::kVRing + kWaves * 16 * D * 4 <= Y::kBytes, "staging fits the V rings");
-    unsigned char* stage = lds + Y::kVRing + wave * (16 * D * 4);
+    constexpr int kC = kRowBytes / 16;      // 16-byte chunks per encoded row
+    constexpr int kRowsPerInst = 64 / kC;   // rows per store instruction
+    static_assert(Y::kVRing + kWaves * 16 * kRowBytes <= Y::kBytes, "staging fits the V rings");
+    unsigned char* stage = lds + Y::kVRing + wave * (16 * kRowBytes);
 #pragma unroll
     for (int k = 0; k < MT; ++k) {
       const int tile = full_tile(k);
       const float lt = group_sum(l_run[k]);
       if (tile >= t_end || (wg != 0 && k >= MTB)) continue;  // (no rows of this wave)
       const float inv = 1.f / lt;
-      // chunk c of row r sits at chunk position c ^ r (conflict-free both ways)
+      float amax = 0.f, sum = 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        *(f32x4*)(stage + l16 * D * 4 + 16 * ((4 * db + grp) ^ (l16 & (kC - 1)))) =
-            acc[k][db] * inv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          amax = fmaxf(amax, __builtin_fabsf(acc[k][db][e]));
+          sum += acc[k][db][e];
+        }
+      const RowCode rc = row_code(group_max(amax) * inv, group_sum(sum) * inv);
+      const float enc = rc.enc * inv;
+      // dims 16 db + 4 grp .. + 3: half (grp & 1) of chunk 2 db + grp / 2, which sits at
+      // chunk position c ^ r in row r (conflict-free both ways)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *(uint2*)(stage + l16 * kRowBytes + 16 * ((2 * db + (grp >> 1)) ^ (l16 & (kC - 1))) +
+                  8 * (grp & 1)) = pack16x4(acc[k][db], enc);
       // (the same wave reads the staging back: its LDS accesses complete in order)
 #pragma unroll
       for (int j = 0; j < 16 / kRowsPerInst; ++j) {
         const int rr = j * kRowsPerInst + lane / kC, c = lane % kC;
-        const f32x4 v = *(const f32x4*)(stage + rr * D * 4 + 16 * (c ^ (rr & (kC - 1))));
-        store24_agent(part_rows, ((tile * 16 + rr) * (3 * D / 4) + 3 * c) * 4, v);
+        const uint4 v = *(const uint4*)(stage + rr * kRowBytes + 16 * (c ^ (rr & (kC - 1))));
+        store_agent(part_rows, (tile * 16 + rr) * kRowBytes + 16 * c, v);
       }
-      if (grp == 0) a.lse_part[slot * G.R_pad + tile * 16 + l16] = (m_ref[k] + __log2f(lt)) * kLn2;
+      if (grp == 0) {
+        lse_rows[tile * 16 + l16] = (m_ref[k] + __log2f(lt)) * kLn2;
+        scale_rows[tile * 16 + l16] = rc.f;
+      }
     }
   }
   if constexpr (LEFT) {
     // Leftover rows: combine the partials of the waves that share a leftover tile (each
     // covered some of its keys) through LDS, as in the merge: M = max m_w, weights 2^(m_w-M).
-    // Every wave is past its loop (barrier above), so the K ring is free.
-    constexpr int kStride = 4 * DB + 2;  // floats per (wave, lane): acc, then m and l
+    // Every wave is past its loop (barrier above), so the K ring is free.  The row's factor
+    // comes from the same combination of the waves' largest magnitudes, a bound on the
+    // combined row's (no larger than the largest |v| the row attends to), so the sharers
+    // need no second exchange.
+    constexpr int kStride = 4 * DB + 4;  // floats per (wave, lane): acc, m, l, max |acc|, sum
+    static_assert(kWaves / 2 * 64 * kStride * 4 <= kKStages * Y::kTileBytes,
+                  "the leftover exchange fits the K ring");
     float* xl = (float*)(lds + Y::kKRing);
-    const float lsum = group_sum(l_l);
     if (has_left) {
+      const float lsum = group_sum(l_l);
+      float amax = 0.f, sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < DB; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          amax = fmaxf(amax, __builtin_fabsf(accl[j][e]));
+          sum += accl[j][e];
+        }
+      amax = group_max(amax);
+      sum = group_sum(sum);
       float* mine = xl + (ww * 64 + lane) * kStride;
 #pragma unroll
       for (int j = 0; j < DB; ++j) *(f32x4*)(mine + 4 * j) = accl[j];
-      mine[4 * DB] = m_refl;
-      mine[4 * DB + 1] = lsum;
+      *(f32x4*)(mine + 4 * DB) = f32x4{m_refl, lsum, amax, sum};
     }
     __syncthreads();
     if (has_left && ltile < t_end) {
@@ -715,21 +748,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
       constexpr int kOwn = DB / kShare;
       const int w0 = NL == 2 ? (ww & ~1) : 0;
       const int o0 = (ww - w0) * kOwn;
-      float mw[kShare], lw[kShare], M = -INFINITY;
+      f32x4 st[kShare];  // (m, l, max |acc|, sum) of each sharer
+      float M = -INFINITY;
 #pragma unroll
       for (int i = 0; i < kShare; ++i) {
-        const float* src = xl + ((w0 + i) * 64 + lane) * kStride;
-        mw[i] = src[4 * DB];
-        lw[i] = src[4 * DB + 1];
-        M = fmaxf(M, mw[i]);
+        st[i] = *(const f32x4*)(xl + ((w0 + i) * 64 + lane) * kStride + 4 * DB);
+        M = fmaxf(M, st[i][0]);
       }
-      float den = 0.f, wgt[kShare];
+      float den = 0.f, bound = 0.f, sum = 0.f, wgt[kShare];
 #pragma unroll
       for (int i = 0; i < kShare; ++i) {
-        wgt[i] = __builtin_amdgcn_exp2f(mw[i] - M);
-        den += wgt[i] * lw[i];
+        wgt[i] = __builtin_amdgcn_exp2f(st[i][0] - M);
+        den += wgt[i] * st[i][1];
+        bound += wgt[i] * st[i][2];
+        sum += wgt[i] * st[i][3];
       }
       const float inv = 1.f / den;
+      const RowCode rc = row_code(bound * inv, sum * inv);
+      const float enc = rc.enc * inv;
       const int row = ltile * 16 + l16;
 #pragma unroll
       for (int j = 0; j < kOwn; ++j) {
@@ -737,9 +773,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
 #pragma unroll
         for (int i = 0; i < kShare; ++i)
           o += wgt[i] * *(const f32x4*)(xl + ((w0 + i) * 64 + lane) * kStride + 4 * (o0 + j));
-        store24_agent(part_rows, (row * (3 * D / 4) + 3 * (4 * (o0 + j) + grp)) * 4, o * inv);
+        store_agent(part_rows, row * kRowBytes + 2 * (16 * (o0 + j) + 4 * grp), pack16x4(o, enc));
       }
-      if (grp == 0 && o0 == 0) a.lse_part[slot * G.R_pad + row] = (M + __log2f(den)) * kLn2;
+      if (grp == 0 && o0 == 0) {
+        lse_rows[row] = (M + __log2f(den)) * kLn2;
+        scale_rows[row] = rc.f;
+      }
     }
   }
 }
@@ -815,6 +854,7 @@ hipError_t launch_prefix_attn_splitk(const Geometry& g, const void* q, const voi
   a.prefix_len = prefix_len;
   a.status_reset = ws.status_reset;
   a.lse_part = ws.lse_part;
+  a.o_scale = ws.o_scale;
   a.o_part = ws.o_part;
   a.g = g;
   int tpb, nb;

@@ -46,7 +46,8 @@ struct TreeArgs {
   int32_t* status;                // [B]
   uint64_t* masks_out;            // [B, T, W] or null
   float* lse_part;
-  uint32_t* o_part;               // packed 24-bit rows (store24)
+  float* o_scale;                 // the factor of each o_part row
+  uint32_t* o_part;               // 16-bit rows (pack16x4)
   Geometry g;
   int32_t attention;              // 0: masks and status only
 };
@@ -169,13 +170,11 @@ __global__ __launch_bounds__(kThreads) void tree_attn_masked(TreeArgs a) {
 
   if (rt >= G.NT) return;
   const size_t slot = ((size_t)b * G.Hkv + kv) * (G.S + 1) + G.S;
-  uint32_t* orow = a.o_part + (slot * G.R_pad + row) * (3 * D / 4);
-  if (tree_bad) {
-    if (row_ok) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        store24(orow, 4 * db + grp, f32x4{NAN, NAN, NAN, NAN});
-      if (grp == 0) a.lse_part[slot * G.R_pad + row] = NAN;
+  uint32_t* orow = a.o_part + (slot * G.R_pad + row) * (D / 2);
+  if (tree_bad) {  // a NaN factor makes the whole row NaN
+    if (row_ok && grp == 0) {
+      a.lse_part[slot * G.R_pad + row] = NAN;
+      a.o_scale[slot * G.R_pad + row] = NAN;
     }
     return;
   }
@@ -258,12 +257,28 @@ __global__ __launch_bounds__(kThreads) void tree_attn_masked(TreeArgs a) {
   }
 
   // ---- normalise and write the tree partial (every real row sees at least itself)
+  // (16-bit values with the row's factor, from its largest magnitude over the 4 lanes
+  // holding it; dims 16 db + 4 grp .. + 3 are dwords 8 db + 2 grp, + 1 of the row)
   const float lt = group_sum(l_run);
+  float amax = 0.f, sum = 0.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      amax = fmaxf(amax, __builtin_fabsf(acc[db][e]));
+      sum += acc[db][e];
+    }
+  amax = group_max(amax);
+  sum = group_sum(sum);
   if (!row_ok) return;
   const float inv = 1.f / lt;
+  const RowCode rc = row_code(amax * inv, sum * inv);
 #pragma unroll
-  for (int db = 0; db < DB; ++db) store24(orow, 4 * db + grp, acc[db] * inv);
-  if (grp == 0) a.lse_part[slot * G.R_pad + row] = (m_run + __log2f(lt)) * kLn2;
+  for (int db = 0; db < DB; ++db) *(uint2*)(orow + 8 * db + 2 * grp) = pack16x4(acc[db], rc.enc * inv);
+  if (grp == 0) {
+    a.lse_part[slot * G.R_pad + row] = (m_run + __log2f(lt)) * kLn2;
+    a.o_scale[slot * G.R_pad + row] = rc.f;
+  }
 }
 
 }  // namespace
@@ -281,6 +296,7 @@ hipError_t launch_tree_attn_masked(const Geometry& g, const void* q, const void*
   a.status = ws.status;
   a.masks_out = masks_out;
   a.lse_part = ws.lse_part;
+  a.o_scale = ws.o_scale;
   a.o_part = ws.o_part;
   a.g = g;
   a.attention = attention ? 1 : 0;
