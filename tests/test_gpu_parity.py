@@ -160,6 +160,55 @@ def test_prefix_partials_match_oracle_per_chunk():
     assert worst_o <= OUT_TOL and worst_l <= LSE_TOL
 
 
+def test_partial_rows_zero_and_wide_range():
+    """The 16-bit partial rows against their contract in include/hta.h, read straight from the
+    workspace: value = q * o_scale with o_scale = m / 32767, m at least the row's largest
+    magnitude and at most the largest |v| the row attends to, and each value within half a
+    step.  A KV head whose V is all zero gives factors of 0 and exact zeros; a KV head whose
+    V dims span six orders of magnitude exercises the bound on the small dims."""
+    gen = torch.Generator().manual_seed(3)
+    par = [W.level_tree(W.LONGSPEC_TREE_WIDTHS, gen) for _ in range(2)]
+    w = _small("partial_rows", par, L=700, plen=[700, 300], seed=3)
+    w.v_prefix[:, 0] = 0
+    dim_scale = torch.logspace(-3, 3, w.head_dim)
+    w.v_prefix[:, 1] = (w.v_prefix[:, 1].float() * dim_scale).to(w.v_prefix.dtype)
+    t = to_dev(w)
+    desc = hta.desc_for(t["q"], t["k_prefix"], w.scale, chunk=256)
+    ws = hta.new_workspace(desc, "cuda")
+    hta.hta_prefix_partials(desc, t["q"], t["k_prefix"], t["v_prefix"], t["prefix_len"], ws)
+    torch.cuda.synchronize()
+    lse_p, o_p = (x.cpu().double().numpy() for x in hta.partial_views(desc, ws))
+    info = hta.plan(desc)
+    S1, Rp = info.num_splits + 1, info.rows_padded
+    n = w.batch * w.num_kv_heads * S1 * Rp
+    fac = ws[info.o_scale_offset:info.o_scale_offset + 4 * n].view(torch.float32)
+    fac = fac.view(w.batch, w.num_kv_heads, S1, Rp).cpu().double().numpy()
+    G = w.num_q_heads // w.num_kv_heads
+    R = w.tree_size * G
+    worst = 0.0
+    for b in range(w.batch):
+        Lb = int(w.prefix_len[b])
+        for s in range((Lb + info.chunk - 1) // info.chunk):
+            assert np.all(fac[b, 0, s, :R] == 0.0) and np.all(o_p[b, 0, s, :R] == 0.0)
+            assert np.all(np.isfinite(lse_p[b, 0, s, :R]))
+            k0, k1 = s * info.chunk, min((s + 1) * info.chunk, Lb)
+            K = w.k_prefix[b, 1, k0:k1].double().numpy()
+            V = w.v_prefix[b, 1, k0:k1].double().numpy()
+            Q = np.stack([w.q[b, r // G, G + r % G].double().numpy() for r in range(R)])
+            ro, _ = oracle.masked_attention(Q, K, V, np.ones((R, k1 - k0), bool), w.scale)
+            # the kernel's own error: the fp16 probabilities move each weight by at most
+            # 2^-11 relative, so a dim's error is at most ~2 * 2^-11 of its largest |v|
+            kern = 2.0 * 2.0 ** -11 * np.max(np.abs(V), axis=0)
+            m = fac[b, 1, s, :R] * 32767.0
+            assert np.all(m >= np.max(np.abs(ro), axis=1) - np.max(kern)), "factor below the row"
+            assert np.all(m <= np.max(np.abs(V)) * (1 + 1e-6)), "factor above max |v|"
+            err = np.abs(o_p[b, 1, s, :R] - ro)
+            bound = kern[None, :] + 0.5 * 1.01 * fac[b, 1, s, :R, None]
+            worst = max(worst, float(np.max(err / bound)))
+    _log(f"  wide-range partial rows: worst error / (kernel + half-step) bound = {worst:.3f}")
+    assert worst <= 1.0
+
+
 def test_merge_matches_oracle_merge_of_gpu_partials():
     """lse_merge against the oracle's merge applied to the very partials the GPU produced."""
     gen = torch.Generator().manual_seed(3)
