@@ -44,7 +44,8 @@
 //    normaliser share the reference.  Probabilities enter the PV product as fp16
 //    (nearest-even, 11 significant bits, at most 2^15), V is widened from bf16 to fp16
 //    (exact for |v| in [2^-14, 65504]), and the normaliser adds those same rounded
-//    probabilities in fp32 (v_dot2 against (1, 1), two per instruction): numerator and
+//    probabilities in fp32 on the matrix core (the PV product with a block of ones in place
+//    of V^T, one more product per row tile and 32 keys, off the VALU): numerator and
 //    normaliser weight every key alike, so a key that dominates its row comes out exact.
 #include "hta_internal.h"
 #include "lds_tiles.h"
@@ -88,18 +89,13 @@ __device__ __forceinline__ i16x4 tr_read_b64(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
 }
 
-// c + the fp16 values of v, added in fp32 two per instruction (v_dot2 against (1, 1))
-__device__ __forceinline__ float add_f16(f16x8 v, float c) {
-  const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
-  c = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 0, 1), one, c, false);
-  c = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 2, 3), one, c, false);
-  c = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 4, 5), one, c, false);
-  return __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 6, 7), one, c, false);
-}
-__device__ __forceinline__ float add_f16(f16x4 v, float c) {
-  const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
-  c = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 0, 1), one, c, false);
-  return __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 2, 3), one, c, false);
+// The A operand of the row-sum product: a 16 x 32 block of ones, so O^T = ones P^T holds in
+// every one of its 16 rows the sum over the 32 keys of each query row's fp16 probabilities.
+__device__ __forceinline__ f16x8 ones_f16x8() {
+  f16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (_Float16)1.f;
+  return v;
 }
 
 __device__ __forceinline__ _Float16 bf16_bits_to_f16(short h) {
@@ -329,10 +325,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
 
   f32x4 acc[MTA][DB];
   f32x4 accl[LEFT ? DB : 1];
-  float l_run[MTA], l_l = 0.f;
+  // running row sums (normalisers), accumulated by the row-sum product: every element of
+  // lsum[k] holds the sum for this lane's query row
+  f32x4 lsum[MTA];
+  f32x4 lsuml = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < MT; ++k) {
-    l_run[k] = 0.f;
+    lsum[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[k][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -460,23 +459,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     constexpr bool WL = decltype(tag)::value;
     constexpr int MTE = decltype(tag)::rows;
     // ---- probabilities against the running reference (fp32), rounded to the fp16 P^T
-    // operands; the row sums add exactly those rounded values (in fp32), so numerator and
-    // normaliser weight every key alike.  ln: the running sum with this half's values.
-    float p[MTA][8], pl[8], ln[MTA], lnl = 0.f, xm[MTA], xml = -INFINITY;
+    // operands; the row-sum product in pv() adds exactly those rounded values (in fp32), so
+    // numerator and normaliser weight every key alike.
+    float p[MTA][8], pl[8], xm[MTA], xml = -INFINITY;
     auto make_ops = [&](int k) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) pop[k][e] = (_Float16)p[k][e];
-      ln[k] = add_f16(pop[k], l_run[k]);
     };
     auto make_left = [&]() {
       if constexpr (LKB == 2) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) popl[e] = (_Float16)pl[e];
-        lnl = add_f16(popl, l_l);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) popl4[e] = (_Float16)pl[e];
-        lnl = add_f16(popl4, l_l);
       }
     };
     // (the exponents' maximum decides the rare reference raise, off the path of the sums)
@@ -524,7 +520,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
         const float shift = mx > kRaiseLog2 ? mx : 0.f;
         const float alpha = __builtin_amdgcn_exp2f(-shift);
         m_ref[k] += shift;
-        l_run[k] *= alpha;
+        lsum[k] *= alpha;
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[k][e] *= alpha;
         make_ops(k);
@@ -537,7 +533,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
           const float shift = mx > kRaiseLog2 ? mx : 0.f;
           const float alpha = __builtin_amdgcn_exp2f(-shift);
           m_refl += shift;
-          l_l *= alpha;
+          lsuml *= alpha;
 #pragma unroll
           for (int e = 0; e < 4 * LKB; ++e) pl[e] *= alpha;
           make_left();
@@ -547,11 +543,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
       }
     }
     // (P^T operand of k-step h: element e <-> key 32 h + 16 (e / 4) + 4 grp + (e % 4))
-#pragma unroll
-    for (int k = 0; k < MTE; ++k) l_run[k] = ln[k];
-    if constexpr (WL) {
-      if (lhere) l_l = lnl;
-    }
   };
 
   // ---- PV(t, h): O^T[d][row] += V^T[d][key] P^T[key][row] for keys 32 h .. 32 h + 31 of tile t
@@ -568,6 +559,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
 #pragma unroll
       for (int k = 0; k < MTE; ++k)
         acc[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[db], pop[k], acc[k][db], 0, 0, 0);
+    // the row sums of the same P^T operands (one product per row tile, no LDS operand)
+#pragma unroll
+    for (int k = 0; k < MTE; ++k)
+      lsum[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones_f16x8(), pop[k], lsum[k], 0, 0, 0);
     // instruction order: operand reads run four d-blocks ahead of the products
     if constexpr (MTE > 0) {
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
@@ -585,6 +580,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
 #pragma unroll
           for (int db = 0; db < DB; ++db)
             accl[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[db], popl, accl[db], 0, 0, 0);
+          lsuml = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones_f16x8(), popl, lsuml, 0, 0, 0);
         } else {
           // the K = 32 product over the whole half with P zero outside this wave's 16-key
           // block (block ljj: the first or second 8-byte half of the operand).  The K = 16
@@ -596,6 +592,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
 #pragma unroll
           for (int db = 0; db < DB; ++db)
             accl[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[db], p8, accl[db], 0, 0, 0);
+          lsuml = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones_f16x8(), p8, lsuml, 0, 0, 0);
         }
       }
     }
@@ -680,7 +677,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
 #pragma unroll
     for (int k = 0; k < MT; ++k) {
       const int tile = full_tile(k);
-      const float lt = group_sum(l_run[k]);
+      const float lt = lsum[k][0];  // (the product summed over all keys of the row)
       if (tile >= t_end || (wg != 0 && k >= MTB)) continue;  // (no rows of this wave)
       const float inv = 1.f / lt;
       float amax = 0.f, sum = 0.f;
@@ -724,7 +721,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
                   "the leftover exchange fits the K ring");
     float* xl = (float*)(lds + Y::kKRing);
     if (has_left) {
-      const float lsum = group_sum(l_l);
+      const float lsumw = lsuml[0];
       float amax = 0.f, sum = 0.f;
 #pragma unroll
       for (int j = 0; j < DB; ++j)
@@ -738,7 +735,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
       float* mine = xl + (ww * 64 + lane) * kStride;
 #pragma unroll
       for (int j = 0; j < DB; ++j) *(f32x4*)(mine + 4 * j) = accl[j];
-      *(f32x4*)(mine + 4 * DB) = f32x4{m_refl, lsum, amax, sum};
+      *(f32x4*)(mine + 4 * DB) = f32x4{m_refl, lsumw, amax, sum};
     }
     __syncthreads();
     if (has_left && ltile < t_end) {
