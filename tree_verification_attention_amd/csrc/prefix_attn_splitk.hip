@@ -610,7 +610,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   //   first group:   [PV(t-1,1) S(t,0)] [softmax(t,0)] [PV(t,0) S(t,1)] [softmax(t,1)]
   //   second group:  [softmax(t-1,1)]   [PV(t-1,1) S(t,0)] [softmax(t,0)] [PV(t,0) S(t,1)]
   // Only the first group carries leftover rows; the second also transposes V in its first
-  // VALU phase.
+  // VALU phase.  With two row tiles per first-group wave (the compute-heavy shapes) the
+  // first group issues tile t+3 after its first softmax of tile t rather than right after
+  // the barrier: its first matrix phase then starts at once, and the loads still run 1.5
+  // tiles ahead of their use (Llama 32k prefix pass -0.6 µs, 262k -2%).  Lighter shapes are
+  // bound by the K/V stream and keep the full two tiles of lead (issuing later cost them
+  // 2-3%).
+  constexpr bool kLateIssue = MT >= 2;  // where the first group issues the next tile loads
   auto run_chunk = [&](auto group) {
     constexpr bool LAG = decltype(group)::value;  // second wave group
     constexpr PassTag<!LAG && LEFT, LAG ? MTB : MT> tag{};
@@ -634,15 +640,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     for (int t = 0; t < ntiles; ++t) {
       // tile t+1 landed (for the transpose), V^T of tile t complete, tile t-1 done
       wait_tiles_and_barrier(min(t + 2, ntiles - 1) - (t + 1));
-      if constexpr (!LAG) {
-        if (t + 3 < ntiles) issue(t + 3);  // refills the K stage of t-1 and the V stage of t
-      } else {
+      if constexpr (LAG) {
         if (t > 0) softmax(tag, 1, sc, scl);
         if (t + 1 < ntiles) transpose_v(t + 1);
+      } else if constexpr (!kLateIssue) {
+        if (t + 3 < ntiles) issue(t + 3);  // refills the K stage of t-1 and the V stage of t
       }
       if (t > 0) pv(tag, t - 1, 1);
       scores(tag, t, 0, sc, scl);
       softmax(tag, 0, sc, scl);
+      if constexpr (!LAG && kLateIssue) {
+        // refills the K stage of t-1 and the V stage of t (free since the barrier)
+        if (t + 3 < ntiles) issue(t + 3);
+      }
       pv(tag, t, 0);
       scores(tag, t, 1, sc, scl);
       if constexpr (!LAG) softmax(tag, 1, sc, scl);
