@@ -823,8 +823,9 @@ hipError_t launch_d(const PrefixArgs& a, RowShape r, dim3 grid, hipStream_t stre
   return hipErrorInvalidValue;
 }
 
-// Matrix-core load of a shape on each SIMD (one wave of each group), in row tiles per key
-// tile: a leftover tile is spread over the four first-group waves.
+// Four times the matrix-core load of a shape on each SIMD (one wave of each group), in row
+// tiles per key tile (a leftover tile is spread over the four first-group waves); equal to
+// the number of row tiles the shape holds.
 constexpr int simd_load4(RowShape r) { return 4 * (r.mt + r.mtb) + r.nl; }
 
 // The shape for `tiles` row tiles: the one that holds them all (4 (MT + MTB) + NL >= tiles)
