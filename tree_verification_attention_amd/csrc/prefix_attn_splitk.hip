@@ -427,31 +427,26 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     }
   };
 
-  // ---- reference of the pass: maximum of the chunk's first 32 keys (tile 0 in LDS; it
-  // always holds a valid key)
-  auto set_reference = [&](auto tag) {
-    constexpr bool WL = decltype(tag)::value;
+  // ---- reference of the pass: maximum of the chunk's first 32 keys, taken from the scores
+  // of tile 0's first half (tile 0 always holds a valid key); for the leftover rows, the
+  // maximum over this wave's first key block(s), in half lh of tile 0
+  auto set_reference = [&](auto tag, const f32x4 (&sc)[MTA][2]) {
     constexpr int MTE = decltype(tag)::rows;
-    f32x4 sc[MTA][2];
-    f32x4 scl[2];
-    scores(tag, 0, 0, sc, scl);
 #pragma unroll
     for (int k = 0; k < MTE; ++k) {
       const float m0 = fmaxf(fmaxf(sc[k][0][0], sc[k][0][1]), fmaxf(sc[k][0][2], sc[k][0][3]));
       const float m1 = fmaxf(fmaxf(sc[k][1][0], sc[k][1][1]), fmaxf(sc[k][1][2], sc[k][1][3]));
       m_ref[k] = group_max(fmaxf(m0, m1) * a.c);
     }
-    if constexpr (WL) {
-      // the leftover reference: the maximum over this wave's first key block(s) of tile 0
-      if (lh != 0) scores(tag, 0, lh, sc, scl);
-      float m = -INFINITY;
+  };
+  auto set_reference_left = [&](const f32x4 (&scl)[2]) {
+    float m = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < LKB; ++i)
-        m = fmaxf(m, fmaxf(fmaxf(scl[i][0], scl[i][1]), fmaxf(scl[i][2], scl[i][3])));
-      m = group_max(m * a.c);
-      // a block wholly past the chunk end leaves no valid key: any finite reference will do
-      m_refl = m == -INFINITY ? 0.f : m;
-    }
+    for (int i = 0; i < LKB; ++i)
+      m = fmaxf(m, fmaxf(fmaxf(scl[i][0], scl[i][1]), fmaxf(scl[i][2], scl[i][3])));
+    m = group_max(m * a.c);
+    // a block wholly past the chunk end leaves no valid key: any finite reference will do
+    m_refl = m == -INFINITY ? 0.f : m;
   };
 
   // ---- softmax of the scores of half h (from scores()): probabilities, P^T operands
@@ -620,20 +615,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   auto run_chunk = [&](auto group) {
     constexpr bool LAG = decltype(group)::value;  // second wave group
     constexpr PassTag<!LAG && LEFT, LAG ? MTB : MT> tag{};
-    // Prologue: tiles 0 and 1 (the first iteration needs both) and the query operands, then
-    // tile 2.  The compiler does not count direct loads, so it would wait for every one of
-    // them (vmcnt(0)) before the first use of the query registers; an explicit full wait
-    // placed before tile 2 is issued lets it stream while tile 0 is consumed.
-    if constexpr (!LAG)
-      for (int t = 0; t < 2 && t < ntiles; ++t) issue(t);
+    // Prologue: the query operands, tiles 0 and 1 (the first iteration needs both), then
+    // tile 2.  The queries go first: every split of the head reads them at the same moment,
+    // and issued behind the tile loads they returned only after the whole first-tile burst
+    // (~1 µs later than the tiles on Llama 32k).  The compiler does not count direct loads,
+    // so it would wait for every one of them (vmcnt(0)) before the first use of the query
+    // registers; an explicit full wait placed before tile 2 is issued lets tile 2 stream
+    // while tile 0 is consumed.  The softmax reference comes from the first scores of the
+    // loop (no separate pass over tile 0).
 #pragma unroll
     for (int k = 0; k < decltype(tag)::rows; ++k) load_q(full_tile(k), qop[k]);
     if constexpr (decltype(tag)::value) load_q(ltile, qopl);
+    if constexpr (!LAG)
+      for (int t = 0; t < 2 && t < ntiles; ++t) issue(t);
     __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
     if constexpr (!LAG)
       if (ntiles > 2) issue(2);
     wait_tiles_and_barrier(min(2, ntiles - 1));
-    set_reference(tag);
     if constexpr (LAG) transpose_v(0);
     f32x4 sc[MTA][2];  // scores of the half in flight (the second group carries them on)
     f32x4 scl[2];
@@ -648,6 +646,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
       }
       if (t > 0) pv(tag, t - 1, 1);
       scores(tag, t, 0, sc, scl);
+      if (t == 0) {
+        set_reference(tag, sc);
+        if constexpr (decltype(tag)::value)
+          if (lh == 0) set_reference_left(scl);
+      }
       softmax(tag, 0, sc, scl);
       if constexpr (!LAG && kLateIssue) {
         // refills the K stage of t-1 and the V stage of t (free since the barrier)
@@ -655,6 +658,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
       }
       pv(tag, t, 0);
       scores(tag, t, 1, sc, scl);
+      if constexpr (decltype(tag)::value)
+        if (t == 0 && lh == 1) set_reference_left(scl);
       if constexpr (!LAG) softmax(tag, 1, sc, scl);
     }
     if constexpr (LAG) softmax(tag, 1, sc, scl);
