@@ -14,8 +14,10 @@
 // splits g, g+4, g+8, ... and each of its lanes owns D/16 consecutive output dimensions
 // (8- or 16-byte loads of the 16-bit partial values), so a group reads whole partial rows;
 // the row's factor (o_scale) and log-sum-exp come with them.  Every load of the
-// first 36 splits (their log-sum-exps and partial rows), the tree part and the sequence's
-// prefix length is issued before any is used, so the merge costs one memory round trip: the
+// first 4 KB splits (their log-sum-exps and partial rows; KB per lane, 1, 2, 4 or 9 by the
+// split count, so few splits hold few registers and more waves stay resident), the tree
+// part and the sequence's prefix length is issued before any is used, so the merge costs
+// one memory round trip: the
 // slots of splits past the prefix end are read speculatively and never used (they
 // contribute through a select, never a multiply by zero, so stale contents are harmless).
 // The four group sums are added across lanes l, l^16, l^32, l^48 and the first group writes
@@ -36,6 +38,8 @@
 // PV product, or a non-finite input) is written as NaN and recorded in the sequence's status
 // (kStatusNonFinite), so such a result is never silently wrong.
 #include "hta_internal.h"
+
+#include <type_traits>
 
 namespace hta {
 
@@ -116,14 +120,14 @@ __device__ inline float group_max4(float x) {
 }
 
 // TIN: element type of q, k_tree, v_tree (unsigned short = bf16 bits, or float)
-template <int D, int MODE, typename TIN>
+template <int D, int MODE, typename TIN, int KB>
 __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   constexpr bool FUSED = MODE != kPlain;   // computes the tree part
   constexpr bool PREFIX = MODE != kTreeOnly;
   constexpr int DPL = D / 16;   // output dimensions per lane of a part group
   constexpr int NW = DPL / 2;   // dwords of 16-bit values per part and lane
   using Sh = Share16<NW>;
-  constexpr int kBatch = 9;     // splits per lane per pass: 36 per pass
+  constexpr int kBatch = KB;    // splits per lane per pass: 4 KB per pass
   __shared__ int32_t s_par[kThreads / 64][kMaxT];  // fused: parent pointers, one slice per wave
   const Geometry& G = a.g;
   const int lane = threadIdx.x & 63;
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   // A wave's loads complete in order.  The fused merge issues the first partials, then the
   // tree rows its row needs (found from the parent pointers, which were issued first), then
   // the remaining partials: the tree part is computed while those are still arriving.
-  constexpr int kEarly = FUSED ? 4 : kBatch;
+  constexpr int kEarly = FUSED ? (kBatch < 4 ? kBatch : 4) : kBatch;
   load_parts(0, kEarly);
 
   // ---- validate
@@ -391,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
 #pragma unroll
   for (int k = 0; k < kBatch; ++k)
     if (pg + 4 * k < nsplit) add_part(lk[k], fk[k], v[k]);
-  // splits beyond the first 36 (long prefixes with many splits)
+  // splits beyond the first 4 KB (long prefixes with many splits)
   for (int p0 = 4 * kBatch + pg; p0 < nsplit; p0 += 4 * kBatch) {
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
@@ -443,12 +447,20 @@ hipError_t launch_merge(const MergeArgs& a, const Geometry& g, hipStream_t strea
   const long nrows = (long)g.B * g.T * g.Hq;
   const int rows_per_block = kThreads / 64;
   dim3 grid((unsigned)((nrows + rows_per_block - 1) / rows_per_block));
-  if (g.D == 128)
-    hipLaunchKernelGGL((lse_merge<128, MODE, TIN>), grid, dim3(kThreads), 0, stream, a);
-  else if (g.D == 64)
-    hipLaunchKernelGGL((lse_merge<64, MODE, TIN>), grid, dim3(kThreads), 0, stream, a);
-  else
-    return hipErrorInvalidValue;
+  // partial loads held per lane: enough for the split count (fewer registers, more waves
+  // resident when there are few splits)
+  auto go = [&](auto kb) {
+    constexpr int KB = decltype(kb)::value;
+    if (g.D == 128)
+      hipLaunchKernelGGL((lse_merge<128, MODE, TIN, KB>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((lse_merge<64, MODE, TIN, KB>), grid, dim3(kThreads), 0, stream, a);
+  };
+  if (g.D != 128 && g.D != 64) return hipErrorInvalidValue;
+  if (MODE == kTreeOnly || g.S <= 4) go(std::integral_constant<int, 1>{});
+  else if (g.S <= 8) go(std::integral_constant<int, 2>{});
+  else if (g.S <= 16) go(std::integral_constant<int, 4>{});
+  else go(std::integral_constant<int, 9>{});
   return hipGetLastError();
 }
 
