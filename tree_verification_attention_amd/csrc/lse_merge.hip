@@ -17,9 +17,9 @@
 // first 4 KB splits (their log-sum-exps and partial rows; KB per lane, 1, 2, 4 or 9 by the
 // split count, so few splits hold few registers and more waves stay resident), the tree
 // part and the sequence's prefix length is issued before any is used, so the merge costs
-// one memory round trip: the
-// slots of splits past the prefix end are read speculatively and never used (they
-// contribute through a select, never a multiply by zero, so stale contents are harmless).
+// one memory round trip: the slots of splits past the prefix end are read speculatively
+// and never used (they contribute through a select, never a multiply by zero, so stale
+// contents are harmless).
 // The four group sums are added across lanes l, l^16, l^32, l^48 and the first group writes
 // the row.
 //
