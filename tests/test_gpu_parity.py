@@ -300,8 +300,10 @@ def test_verify_tree_sizes(T):
     check_rows(w, out, lse, n_rows=4000)
 
 
-@pytest.mark.parametrize("chunk", [64, 192, 1024, 4096])
+@pytest.mark.parametrize("chunk", [64, 192, 320, 448, 1024, 4096])
 def test_verify_chunk_sizes_all_within_tolerance(chunk):
+    """2999 keys in 47, 16, 10, 7, 3 and 1 splits: every size of the merge's per-lane batch
+    of partials (9, 4, 4, 2, 1, 1 splits per lane) and its pass beyond the first batch."""
     gen = torch.Generator().manual_seed(7)
     par = [W.level_tree(W.LONGSPEC_TREE_WIDTHS, gen)]
     w = _small("chunks", par, B=1, Hq=8, Hkv=2, L=3000, plen=[2999], seed=7)
