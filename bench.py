@@ -275,17 +275,24 @@ SQ_PASSES = (
     "SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL SQ_INSTS_VALU SQ_INSTS_MFMA",
     "SQ_CYCLES SQ_WAVES SQ_INSTS_LDS SQ_INSTS_SALU SQ_ACTIVE_INST_SCA SQ_ACTIVE_INST_VMEM "
     "SQ_INST_LEVEL_LDS SQ_ACTIVE_INST_MISC",
+    "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_LDS_IDX_ACTIVE "
+    "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE GRBM_COUNT",
 )
+# GRBM counters are summed over the chip's XCDs (one instance each)
+XCDS = 8
 
 
 def summarize_sq(workload: str, dirs) -> str:
-    """SQ counters of the prefix kernel from three rocprofv3 --pmc passes (SQ_PASSES, each on
-    --mode prefix-only) as a markdown table plus the per-wave and per-SIMD ratios."""
+    """SQ counters of the prefix kernel from the rocprofv3 --pmc passes of SQ_PASSES (each on
+    --mode prefix-only) as a markdown table plus the per-wave and per-SIMD ratios; with the
+    fourth pass also the matrix-core and LDS utilisation over the kernel's active cycles and
+    the matrix-core flops executed against the algorithmic ones."""
     kern = "prefix_attn_splitk"
     vals = {}
-    for d, counters in zip(dirs, SQ_PASSES):
+    for i, (d, counters) in enumerate(zip(dirs, SQ_PASSES)):
         for c in counters.split():
-            vals[c] = _counter_means(d, kern, c)[0]
+            key = c if i < 3 or c not in vals else c + " (4th pass)"
+            vals[key] = _counter_means(d, kern, c)[0]
     waves = vals["SQ_WAVES"]
     per = lambda c: vals[c] / waves  # noqa: E731
     life = per("SQ_WAVE_CYCLES")
@@ -296,8 +303,8 @@ def summarize_sq(workload: str, dirs) -> str:
         f"--workload {workload} --mode prefix-only --steps 10 --warmup 2"
         for d, c in zip(dirs, SQ_PASSES))
     lines = [f"# SQ counters: prefix_attn_splitk, {workload}", "",
-             "Commands (from the repository root, on one MI355X; three passes of at most eight "
-             "SQ counters each), then `python3 bench.py --workload " + workload +
+             f"Commands (from the repository root, on one MI355X; {len(dirs)} passes of at most "
+             "eight SQ and two GRBM counters each), then `python3 bench.py --workload " + workload +
              " --summarize-sq " + " ".join(dirs) + "`:", "", "```",
              "cd /tmp && export TMPDIR=/tmp && cd -", cmds, "```", "",
              f"Kernel source sha256[:16] = `{kernel_source_hash()}`.  Values: per dispatch, "
@@ -316,6 +323,20 @@ def summarize_sq(workload: str, dirs) -> str:
               f"{per('SQ_INSTS_VALU'):,.0f} VALU (MFMA included), {per('SQ_INSTS_LDS'):,.0f} LDS, "
               f"{per('SQ_INSTS_SALU'):,.0f} SALU; LDS bank-conflict cycles "
               f"{per('SQ_LDS_BANK_CONFLICT'):,.0f} per wave."]
+    if "GRBM_GUI_ACTIVE" in vals:
+        active = vals["GRBM_GUI_ACTIVE"] / XCDS  # the kernel's active cycles (one XCD's count)
+        busy4 = vals.get("SQ_VALU_MFMA_BUSY_CYCLES (4th pass)", vals["SQ_VALU_MFMA_BUSY_CYCLES"])
+        mops = vals["SQ_INSTS_VALU_MFMA_MOPS_BF16"] + vals["SQ_INSTS_VALU_MFMA_MOPS_F16"]
+        alg = alg_figures(W.by_name(workload))["prefix_flops"]
+        lines += ["",
+                  f"Over the kernel's active cycles (GRBM_GUI_ACTIVE / {XCDS} XCDs = {active:,.0f} "
+                  f"cycles per dispatch): matrix core busy {busy4 / (active * simds):.0%} of SIMD "
+                  f"cycles; LDS busy (SQ_LDS_IDX_ACTIVE) {vals['SQ_LDS_IDX_ACTIVE'] / (active * 256):.0%} "
+                  f"of CU cycles.  Matrix-core flops executed (MFMA MOPS x 512: bf16 "
+                  f"{vals['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.2f} G, fp16 "
+                  f"{vals['SQ_INSTS_VALU_MFMA_MOPS_F16'] * 512 / 1e9:.2f} G) = {mops * 512 / alg:.3f}x "
+                  f"the pass's algorithmic {alg / 1e9:.2f} GFLOP (row-sum products, padded rows and "
+                  f"the zero half of the leftover products included)."]
     out = os.path.join(PROFILE_DIR, f"prefix_attn_splitk_{workload}_sq_counters.md")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -609,9 +630,10 @@ def main() -> int:
     ap.add_argument("--settle", type=float, default=0.5,
                     help="seconds of untimed steps before the warm-up, so the engine clock is "
                          "at its steady state under this load")
-    ap.add_argument("--summarize-sq", nargs=3, metavar="DIR",
-                    help="write the prefix kernel's SQ counters from the three rocprofv3 --pmc "
-                         "passes of SQ_PASSES into profiles/ and exit; needs no GPU")
+    ap.add_argument("--summarize-sq", nargs="+", metavar="DIR",
+                    help="write the prefix kernel's SQ counters from the rocprofv3 --pmc passes "
+                         "of SQ_PASSES (three or all four, in order) into profiles/ and exit; "
+                         "needs no GPU")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "COMMAND"),
                     help="write a kernel-trace summary of --workload from a rocprofv3 "
                          "--kernel-trace --stats output folder into profiles/ and exit")
