@@ -34,8 +34,12 @@ from .binding import (  # noqa: F401
     new_workspace,
     partial_views,
     plan,
+    prepare_accept_commit,
+    prepare_chunk_mass,
+    prepare_cross_attention,
     prepare_merge,
     prepare_prefix_partials,
+    prepare_rope_tree,
     prepare_tree_partials,
     prepare_verify,
     rope_tree,
@@ -51,7 +55,8 @@ __all__ = [
     "hta_window_commit", "hta_accept_commit", "hta_ancestor_masks", "hta_chunk_mass",
     "hta_dense_mask", "hta_verify_dense", "verify_dense", "hta_get_device_status", "hta_merge",
     "hta_prefix_partials", "hta_rope_tree", "hta_tree_partials", "hta_verify", "hta_verify_noalloc", "load",
-    "make_desc", "new_workspace", "partial_views", "plan", "prepare_merge",
-    "prepare_prefix_partials", "prepare_tree_partials", "prepare_verify", "rope_tree", "status_str", "verify",
+    "make_desc", "new_workspace", "partial_views", "plan", "prepare_accept_commit",
+    "prepare_chunk_mass", "prepare_cross_attention", "prepare_merge", "prepare_prefix_partials",
+    "prepare_rope_tree", "prepare_tree_partials", "prepare_verify", "rope_tree", "status_str", "verify",
     "workspace_size",
 ]

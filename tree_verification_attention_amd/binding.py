@@ -151,6 +151,17 @@ def _check(code: int, what: str) -> None:
         raise HtaError(code, what)
 
 
+def _enqueue(fn, args, keep, what: str):
+    """A callable that enqueues fn(*args) again on every call (arguments checked and marshalled
+    once by the caller); keep holds the buffers alive as long as the callable."""
+    def call() -> None:
+        code = fn(*args)
+        if code != 0:
+            raise HtaError(code, what)
+    call.keep = keep
+    return call
+
+
 def make_desc(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, tree_size: int,
               max_prefix_len: int, in_dtype: int = HTA_BF16, scale: float = 0.0,
               chunk: int = 0) -> hta_desc:
@@ -433,28 +444,42 @@ def hta_get_device_status(desc, workspace, stream=None) -> Tuple[int, int]:
     return int(code), int(bad.value)
 
 
-def hta_chunk_mass(desc, prefix_len, lse, mass, chunk_scores, workspace, stream=None) -> None:
+def prepare_chunk_mass(desc, prefix_len, lse, mass, chunk_scores, workspace, stream=None):
+    """hta_chunk_mass checked and marshalled once (see prepare_verify)."""
     B, T, Hq, Hkv, D, L = _dims(desc)
     S1 = plan(desc).num_splits + 1
     _validate([("prefix_len", prefix_len, (B,), _I32), ("lse", lse, (B, Hq, T), _F32),
                ("mass", mass, (B, Hq, T, S1), _F32),
                ("chunk_scores", chunk_scores, (B, S1), _F32)], workspace, workspace_size(desc))
-    _check(load().hta_chunk_mass(ctypes.byref(desc), _ptr(prefix_len), _ptr(lse), _ptr(mass),
-                                 _ptr(chunk_scores), _ptr(workspace), workspace.numel(),
-                                 _stream(stream)), "hta_chunk_mass")
+    args = (ctypes.byref(desc), _ptr(prefix_len), _ptr(lse), _ptr(mass), _ptr(chunk_scores),
+            _ptr(workspace), workspace.numel(), _stream(stream))
+    return _enqueue(load().hta_chunk_mass, args,
+                    (desc, prefix_len, lse, mass, chunk_scores, workspace), "hta_chunk_mass")
 
 
-def hta_cross_attention(desc, q, k_cache, v_cache, cache_len, out, lse, workspace,
-                        stream=None) -> None:
+def hta_chunk_mass(desc, prefix_len, lse, mass, chunk_scores, workspace, stream=None) -> None:
+    prepare_chunk_mass(desc, prefix_len, lse, mass, chunk_scores, workspace, stream)()
+
+
+def prepare_cross_attention(desc, q, k_cache, v_cache, cache_len, out, lse, workspace,
+                            stream=None):
+    """hta_cross_attention checked and marshalled once (see prepare_verify)."""
     B, T, Hq, Hkv, D, L = _dims(desc)
     X = _in_dtype(desc)
     _validate([("q", q, (B, T, Hq, D), X), ("k_cache", k_cache, (B, Hkv, L, D), X),
                ("v_cache", v_cache, (B, Hkv, L, D), X), ("cache_len", cache_len, (B,), _I32),
                ("out", out, (B, T, Hq, D), _F32), ("lse", lse, (B, Hq, T), _F32)],
               workspace, workspace_size(desc))
-    _check(load().hta_cross_attention(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                      _ptr(cache_len), _ptr(out), _ptr(lse), _ptr(workspace),
-                                      workspace.numel(), _stream(stream)), "hta_cross_attention")
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len),
+            _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream))
+    return _enqueue(load().hta_cross_attention, args,
+                    (desc, q, k_cache, v_cache, cache_len, out, lse, workspace),
+                    "hta_cross_attention")
+
+
+def hta_cross_attention(desc, q, k_cache, v_cache, cache_len, out, lse, workspace,
+                        stream=None) -> None:
+    prepare_cross_attention(desc, q, k_cache, v_cache, cache_len, out, lse, workspace, stream)()
 
 
 def cross_attention(q, k_cache, v_cache, cache_len, *, scale=None, chunk: int = 0,
@@ -550,26 +575,36 @@ def chunk_mass(desc, prefix_len, lse, workspace, stream=None):
     return mass, scores
 
 
-def hta_rope_tree(desc, rope_theta: float, interleaved: bool, q, k_tree, parent_idx, prefix_len,
-                  positions, workspace, stream=None) -> None:
+def prepare_rope_tree(desc, rope_theta: float, interleaved: bool, q, k_tree, parent_idx,
+                      prefix_len, positions, workspace, stream=None):
+    """hta_rope_tree checked and marshalled once (see prepare_verify)."""
     B, T, Hq, Hkv, D, L = _dims(desc)
     X = _in_dtype(desc)
     _validate([("q", q, (B, T, Hq, D), X), ("k_tree", k_tree, (B, Hkv, T, D), X),
                ("parent_idx", parent_idx, (B, T), _I32), ("prefix_len", prefix_len, (B,), _I32),
                ("positions", positions, (B, T), _I32)], workspace, 4 * B)
-    _check(load().hta_rope_tree(ctypes.byref(desc), float(rope_theta), 1 if interleaved else 0,
-                                _ptr(q), _ptr(k_tree), _ptr(parent_idx), _ptr(prefix_len),
-                                _ptr(positions), _ptr(workspace), workspace.numel(),
-                                _stream(stream)), "hta_rope_tree")
+    args = (ctypes.byref(desc), float(rope_theta), 1 if interleaved else 0, _ptr(q),
+            _ptr(k_tree), _ptr(parent_idx), _ptr(prefix_len), _ptr(positions), _ptr(workspace),
+            workspace.numel(), _stream(stream))
+    return _enqueue(load().hta_rope_tree, args,
+                    (desc, q, k_tree, parent_idx, prefix_len, positions, workspace),
+                    "hta_rope_tree")
+
+
+def hta_rope_tree(desc, rope_theta: float, interleaved: bool, q, k_tree, parent_idx, prefix_len,
+                  positions, workspace, stream=None) -> None:
+    prepare_rope_tree(desc, rope_theta, interleaved, q, k_tree, parent_idx, prefix_len,
+                      positions, workspace, stream)()
 
 
 def accept_workspace_size(desc: hta_desc, vocab: int) -> int:
     return int(load().hta_accept_workspace_size(ctypes.byref(desc), int(vocab)))
 
 
-def hta_accept_commit(desc, logits, tokens, root_token, parent_idx, prefix_len, k_prefix,
-                      v_prefix, k_tree, v_tree, target_next, accept_len, accepted, bonus_token,
-                      workspace, stream=None) -> None:
+def prepare_accept_commit(desc, logits, tokens, root_token, parent_idx, prefix_len, k_prefix,
+                          v_prefix, k_tree, v_tree, target_next, accept_len, accepted,
+                          bonus_token, workspace, stream=None):
+    """hta_accept_commit checked and marshalled once (see prepare_verify)."""
     B, T, Hq, Hkv, D, L = _dims(desc)
     X = _in_dtype(desc)
     vocab = logits.shape[-1] if isinstance(logits, torch.Tensor) and logits.dim() == 3 else 0
@@ -581,13 +616,22 @@ def hta_accept_commit(desc, logits, tokens, root_token, parent_idx, prefix_len, 
                ("target_next", target_next, (B, T), _I32), ("accept_len", accept_len, (B,), _I32),
                ("accepted", accepted, (B, T), _I32), ("bonus_token", bonus_token, (B,), _I32)],
               workspace, accept_workspace_size(desc, max(vocab, 1)))
-    _check(load().hta_accept_commit(ctypes.byref(desc), int(vocab), _dtype_code(logits),
-                                    _ptr(logits), _ptr(tokens), _ptr(root_token),
-                                    _ptr(parent_idx), _ptr(prefix_len), _ptr(k_prefix),
-                                    _ptr(v_prefix), _ptr(k_tree), _ptr(v_tree),
-                                    _ptr(target_next), _ptr(accept_len), _ptr(accepted),
-                                    _ptr(bonus_token), _ptr(workspace), workspace.numel(),
-                                    _stream(stream)), "hta_accept_commit")
+    args = (ctypes.byref(desc), int(vocab), _dtype_code(logits), _ptr(logits), _ptr(tokens),
+            _ptr(root_token), _ptr(parent_idx), _ptr(prefix_len), _ptr(k_prefix),
+            _ptr(v_prefix), _ptr(k_tree), _ptr(v_tree), _ptr(target_next), _ptr(accept_len),
+            _ptr(accepted), _ptr(bonus_token), _ptr(workspace), workspace.numel(),
+            _stream(stream))
+    keep = (desc, logits, tokens, root_token, parent_idx, prefix_len, k_prefix, v_prefix,
+            k_tree, v_tree, target_next, accept_len, accepted, bonus_token, workspace)
+    return _enqueue(load().hta_accept_commit, args, keep, "hta_accept_commit")
+
+
+def hta_accept_commit(desc, logits, tokens, root_token, parent_idx, prefix_len, k_prefix,
+                      v_prefix, k_tree, v_tree, target_next, accept_len, accepted, bonus_token,
+                      workspace, stream=None) -> None:
+    prepare_accept_commit(desc, logits, tokens, root_token, parent_idx, prefix_len, k_prefix,
+                          v_prefix, k_tree, v_tree, target_next, accept_len, accepted,
+                          bonus_token, workspace, stream)()
 
 
 # ----------------------------------------------------------------------------- convenience
