@@ -377,6 +377,28 @@ def test_late_score_spikes(D, Hq, Hkv):
         check_rows(w, out, lse)
 
 
+@pytest.mark.parametrize("chunk,Lmax,plen", [
+    # chunks whose first two tiles run past the prefix end (loaded before the length is known,
+    # then loaded again with the rows past the end replaced): 70, 1, 127 and 100 keys in the
+    # last chunk; a full cache; a last chunk too close to Lmax for the early loads
+    (1024, 4096, [1024 + 70, 2048 + 1, 3072 + 127, 100, 4096]),
+    (256, 1500, [256 + 64, 512 + 65, 1, 1500, 1280 + 127]),
+    (128, 700, [128, 129, 640 + 1, 700, 63]),
+])
+def test_prefix_end_inside_first_tiles(chunk, Lmax, plen):
+    """Prefix ends inside a chunk's first two 64-key tiles, with NaN in every cache row past
+    the end: those rows are never read (a NaN V row times a zero probability would poison
+    the row), for several chunk sizes and ragged lengths."""
+    gen = torch.Generator().manual_seed(chunk)
+    par = [W.level_tree((2, 3), gen) for _ in range(len(plen))]
+    w = W.make_workload(f"prefix_end_{chunk}", batch=len(plen), num_q_heads=8, num_kv_heads=2,
+                        head_dim=128, max_prefix_len=Lmax, parents=par, prefix_len=plen,
+                        poison_padding=True, peaky_frac=0.02, seed=chunk + 5)
+    _log(f"prefix end inside the first tiles: chunk={chunk} Lmax={Lmax} plen={plen}")
+    out, lse = run_gpu(w, chunk=chunk)
+    check_rows(w, out, lse)
+
+
 def test_empty_and_tiny_prefixes():
     gen = torch.Generator().manual_seed(8)
     par = [W.level_tree((2, 3), gen) for _ in range(4)]

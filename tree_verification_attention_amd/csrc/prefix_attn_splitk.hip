@@ -205,12 +205,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   const int grp = lane >> 4;
 
   if (a.status_reset && s == 0 && kv == 0 && rb == 0 && threadIdx.x == 0) a.status_reset[b] = 0;
-  int Lb = a.prefix_len[b];
-  Lb = Lb < 0 ? 0 : (Lb > G.Lmax ? G.Lmax : Lb);  // out-of-range lengths are flagged elsewhere
   const int kbeg = s * G.chunk;
-  if (kbeg >= Lb) return;  // empty chunk: the merge never reads this slot
-  const int kend = min(kbeg + G.chunk, Lb);
-  const int ntiles = (kend - kbeg + kKeyTile - 1) / kKeyTile;
+  // set once the prefix length is known
+  int kend = kbeg + 2 * kKeyTile, ntiles = 0;
 
   const size_t kv_base = ((size_t)b * G.Hkv + kv) * (size_t)G.Lmax * D;
   const unsigned short* Kg = a.k_prefix + kv_base;
@@ -252,6 +249,42 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
                       lds + Y::kKRing + (t % kKStages) * Y::kTileBytes,
                       lds + Y::kVRing + (t % kVStages) * Y::kTileBytes, ww, lane);
   };
+
+  // ---- before the prefix length is known: the query operands of this wave's row tiles, and
+  // (first group) tiles 0 and 1 of the chunk as whole tiles, when they lie inside the
+  // cache's allocation.  They are checked against the length once it arrives.
+  if (wg == 0) {
+#pragma unroll
+    for (int k = 0; k < MT; ++k) load_q(full_tile(k), qop[k]);
+    if constexpr (LEFT) load_q(ltile, qopl);
+  } else {
+#pragma unroll
+    for (int k = 0; k < MTB; ++k) load_q(full_tile(k), qop[k]);
+  }
+  const bool early = G.chunk >= 2 * kKeyTile && kbeg + 2 * kKeyTile <= G.Lmax;
+  if (early && wg == 0) {
+    issue(0);
+    issue(1);
+  }
+  // The prefix length is read only now, by a scalar load (b is wave-uniform), so neither
+  // its round trip nor the wait for it delays the loads above, which do not depend on it
+  // (the compiler barrier keeps them in front).
+  asm volatile("" ::: "memory");
+  const int Lraw = *(const __attribute__((address_space(4))) int32_t*)(a.prefix_len + b);
+  int Lb = Lraw < 0 ? 0 : (Lraw > G.Lmax ? G.Lmax : Lraw);  // bad lengths are flagged elsewhere
+  if (kbeg >= Lb) {  // empty chunk: the merge never reads this slot
+    // (no direct load may land in LDS after the workgroup ends)
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+    return;
+  }
+  kend = min(kbeg + G.chunk, Lb);
+  ntiles = (kend - kbeg + kKeyTile - 1) / kKeyTile;
+  if (early && wg == 0 && kend < kbeg + 2 * kKeyTile) {
+    // the early tiles reach past the prefix end (whose rows are never read): once they have
+    // landed, load them again with the rows past the end replaced
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+    for (int t = 0; t < 2 && t < ntiles; ++t) issue(t);
+  }
 
   // ---- V (bf16, keys x d) -> V^T (fp16, d x keys in P^T operand order).  Lane (grp, l16)
   // of (d block db, 32-key half ks) produces d = 16 db + l16, keys 32 ks + 16 (e/4) +
@@ -623,11 +656,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     // registers; an explicit full wait placed before tile 2 is issued lets tile 2 stream
     // while tile 0 is consumed.  The softmax reference comes from the first scores of the
     // loop (no separate pass over tile 0).
-#pragma unroll
-    for (int k = 0; k < decltype(tag)::rows; ++k) load_q(full_tile(k), qop[k]);
-    if constexpr (decltype(tag)::value) load_q(ltile, qopl);
+    // (the query loads, and tiles 0 and 1 where the chunk allows, were issued before the
+    // prefix length arrived)
     if constexpr (!LAG)
-      for (int t = 0; t < 2 && t < ntiles; ++t) issue(t);
+      if (!early)
+        for (int t = 0; t < 2 && t < ntiles; ++t) issue(t);
     __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
     if constexpr (!LAG)
       if (ntiles > 2) issue(2);
