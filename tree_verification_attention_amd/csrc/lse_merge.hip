@@ -130,19 +130,25 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
   constexpr int kBatch = KB;    // splits per lane per pass: 4 KB per pass
   __shared__ int32_t s_par[kThreads / 64][kMaxT];  // fused: parent pointers, one slice per wave
   const Geometry& G = a.g;
+  // (one field of each 64-byte line of the arguments: all three lines come in the first batch
+  // of scalar loads, where the compiler would otherwise fetch them in dependent rounds around
+  // the row test below)
+  asm volatile("" ::"s"(a.prefix_len), "s"(a.q), "s"(a.g.R_pad));
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform, and the row index 32-bit (the launch checks B T Hq < 2^31): the index
+  // arithmetic is a few scalar instructions instead of 64-bit divisions on every lane in
+  // front of the first load
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int pg = lane >> 4, dl = lane & 15;
-  const long row_id = (long)blockIdx.x * (kThreads / 64) + wave;
-  const long nrows = (long)G.B * G.T * G.Hq;
-  if (row_id >= nrows) return;
-  const int h = (int)(row_id % G.Hq);
-  const int i = (int)((row_id / G.Hq) % G.T);
-  const int b = (int)(row_id / ((long)G.Hq * G.T));
+  const int row_id = (int)blockIdx.x * (kThreads / 64) + wave;
+  if (row_id >= G.B * G.T * G.Hq) return;
+  const int h = row_id % G.Hq;
+  const int i = (row_id / G.Hq) % G.T;
+  const int b = row_id / (G.Hq * G.T);
   const int kv = h / G.G;
   const int r = i * G.G + (h % G.G);
   const int T = G.T;
-  float* outp = a.out + row_id * D + DPL * dl;
+  float* outp = a.out + (size_t)row_id * D + DPL * dl;
   float* lsep = a.lse + ((size_t)b * G.Hq + h) * T + i;
   const size_t base = ((size_t)b * G.Hkv + kv) * (G.S + 1);
   const float* lrow = a.lse_part + base * G.R_pad + r;                 // slot s at s * R_pad
@@ -445,6 +451,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge(MergeArgs a) {
 template <int MODE, typename TIN>
 hipError_t launch_merge(const MergeArgs& a, const Geometry& g, hipStream_t stream) {
   const long nrows = (long)g.B * g.T * g.Hq;
+  if (nrows > 0x7fffffffL - kThreads) return hipErrorInvalidValue;  // (32-bit row indices)
   const int rows_per_block = kThreads / 64;
   dim3 grid((unsigned)((nrows + rows_per_block - 1) / rows_per_block));
   // partial loads held per lane: enough for the split count (fewer registers, more waves

@@ -204,7 +204,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   const int l16 = lane & 15;
   const int grp = lane >> 4;
 
-  if (a.status_reset && s == 0 && kv == 0 && rb == 0 && threadIdx.x == 0) a.status_reset[b] = 0;
   const int kbeg = s * G.chunk;
   // set once the prefix length is known
   int kend = kbeg + 2 * kKeyTile, ntiles = 0;
@@ -270,6 +269,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
   // its round trip nor the wait for it delays the loads above, which do not depend on it
   // (the compiler barrier keeps them in front).
   asm volatile("" ::: "memory");
+  // (the status reset goes behind the loads: the wave that stores it would otherwise wait for
+  // the store before issuing them)
+  if (a.status_reset && s == 0 && kv == 0 && rb == 0 && threadIdx.x == 0) a.status_reset[b] = 0;
   const int Lraw = *(const __attribute__((address_space(4))) int32_t*)(a.prefix_len + b);
   int Lb = Lraw < 0 ? 0 : (Lraw > G.Lmax ? G.Lmax : Lraw);  // bad lengths are flagged elsewhere
   if (kbeg >= Lb) {  // empty chunk: the merge never reads this slot
