@@ -19,6 +19,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -130,9 +131,26 @@ def alg_figures(w: W.Workload):
                 kv_units=Hkv * sum_L)
 
 
+KERNEL_HEADERS = [os.path.join(os.path.dirname(KERNEL_SRC), h)
+                  for h in ("hta_internal.h", "lds_tiles.h")]
+
+
+def code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed (string literals are not
+    special-cased: the kernel sources hold none with comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the prefix kernel's code (its source and the two headers it includes, comments
+    and layout ignored): the committed counters are reported only for this code."""
+    h = hashlib.sha256()
+    for path in [KERNEL_SRC, *KERNEL_HEADERS]:
+        with open(path, encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload: str):
@@ -307,7 +325,7 @@ def summarize_sq(workload: str, dirs) -> str:
              "eight SQ and two GRBM counters each), then `python3 bench.py --workload " + workload +
              " --summarize-sq " + " ".join(dirs) + "`:", "", "```",
              "cd /tmp && export TMPDIR=/tmp && cd -", cmds, "```", "",
-             f"Kernel source sha256[:16] = `{kernel_source_hash()}`.  Values: per dispatch, "
+             f"Kernel code sha256[:16] (source and included headers, comments ignored) = `{kernel_source_hash()}`.  Values: per dispatch, "
              "summed over the chip's counter instances, averaged over the sampled dispatches.",
              "", "| Counter | Per dispatch |", "|---|---:|"]
     for c in sorted(vals):

@@ -651,15 +651,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_attn_splitk(PrefixArgs a) 
     constexpr bool LAG = decltype(group)::value;  // second wave group
     constexpr PassTag<!LAG && LEFT, LAG ? MTB : MT> tag{};
     // Prologue: the query operands, tiles 0 and 1 (the first iteration needs both), then
-    // tile 2.  The queries go first: every split of the head reads them at the same moment,
-    // and issued behind the tile loads they returned only after the whole first-tile burst
-    // (~1 µs later than the tiles on Llama 32k).  The compiler does not count direct loads,
-    // so it would wait for every one of them (vmcnt(0)) before the first use of the query
-    // registers; an explicit full wait placed before tile 2 is issued lets tile 2 stream
-    // while tile 0 is consumed.  The softmax reference comes from the first scores of the
-    // loop (no separate pass over tile 0).
-    // (the query loads, and tiles 0 and 1 where the chunk allows, were issued before the
-    // prefix length arrived)
+    // tile 2.  The queries and, where the chunk allows, tiles 0 and 1 were issued before the
+    // prefix length arrived, queries first: every split of the head reads them at the same
+    // moment, and issued behind the tile loads they returned only after the whole first-tile
+    // burst (~1 µs later than the tiles on Llama 32k).  The compiler does not count direct
+    // loads, so it would wait for every one of them (vmcnt(0)) before the first use of the
+    // query registers; an explicit full wait placed before tile 2 is issued lets tile 2
+    // stream while tile 0 is consumed.  The softmax reference comes from the first scores of
+    // the loop (no separate pass over tile 0).
     if constexpr (!LAG)
       if (!early)
         for (int t = 0; t < 2 && t < ntiles; ++t) issue(t);
