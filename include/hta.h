@@ -45,7 +45,9 @@
  * with hta_get_device_status().
  *
  * Limits: head_dim in {64, 128}; 1 <= tree_size <= 256; num_q_heads % num_kv_heads == 0;
- * num_q_heads / num_kv_heads <= 16; every tensor pointer 16-byte aligned, the workspace
+ * num_q_heads / num_kv_heads <= 16; batch <= 65535; batch * tree_size * num_q_heads < 2^31
+ * - 1024; num_kv_heads times the query-row blocks (ceil(tree_size * group / 272), at most 16)
+ * <= 65535; every tensor pointer 16-byte aligned, the workspace
  * 256-byte aligned.  in_dtype HTA_BF16 runs the matrix-core kernels (bf16 products, fp32
  * accumulation, probabilities entering the PV product as fp16 and normalised by the sum of
  * those same rounded values, so a prefix part's log-sum-exp is within 2^-11 of the exact

@@ -114,6 +114,9 @@ def test_partial_views_decode_the_documented_encoding():
     (dict(chunk=100), SHAPE),               # not a multiple of 64
     (dict(scale=-1.0), SHAPE),
     (dict(scale=float("nan")), SHAPE),
+    (dict(batch=65536), SHAPE),                                  # a grid dimension
+    (dict(batch=40000, tree_size=256, num_q_heads=256, num_kv_heads=16), SHAPE),  # 2^31 rows
+    (dict(num_q_heads=16 * 65536, num_kv_heads=65536), SHAPE),   # KV heads x row blocks
     (dict(in_dtype=2), DTYPE),
     (dict(in_dtype=7), DTYPE),
 ])
@@ -121,6 +124,12 @@ def test_bad_descriptors_are_rejected(kw, code):
     d = _desc(**kw)
     assert _plan_code(d) == code
     assert hta.workspace_size(d) == 0
+
+
+def test_launch_limits_admit_their_edges():
+    # the largest batch, and a row count just under the merge's 32-bit limit
+    assert _plan_code(_desc(batch=65535, tree_size=1, num_q_heads=1, num_kv_heads=1)) == 0
+    assert _plan_code(_desc(batch=32767, tree_size=256, num_q_heads=256, num_kv_heads=16)) == 0
 
 
 def test_fp32_inputs_plan_like_bf16():

@@ -56,6 +56,12 @@ hta_status make_plan(const hta_desc* d, Geometry* g, hta_plan_info* info) {
   int tpb, nb;
   hta::prefix_row_blocking(G, &tpb, &nb);
   const int64_t row_blocks = nb;
+  // Launch limits, checked before anything is enqueued: the batch and the KV heads times row
+  // blocks are grid dimensions (at most 65535 each), and the merge numbers its B*T*Hq output
+  // rows with 32-bit integers.
+  if (G.B > 65535 || G.Hkv * row_blocks > 65535 ||
+      (int64_t)G.B * G.T * G.Hq > (int64_t)INT32_MAX - 1024)
+    return HTA_ERR_SHAPE;
   int64_t chunk = d->chunk;
   if (chunk == 0) {
     // As many splits as keep every CU busy without a second partial wave of workgroups:
