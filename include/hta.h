@@ -397,6 +397,19 @@ hta_status hta_accept_commit(const hta_desc *desc, int32_t vocab, int32_t logits
 hta_status hta_get_device_status(const hta_desc *desc, const void *workspace, void *stream,
                                  int32_t *bad_sequence);
 
+/* Measurement helper, not part of the verification path: the matrix-core rate this GPU
+ * sustains, for reporting the prefix pass against a peak measured on the machine (the pages
+ * give no hardware; the data-sheet peak assumes clocks a part may not hold under matrix load).
+ * Enqueues on `stream` one launch of `blocks` workgroups of 8 waves; every wave runs `iters`
+ * rounds of eight independent v_mfma_f32_16x16x32_bf16 products on register operands (no
+ * memory traffic), then writes one float per lane to `out` (device, blocks * 512 floats,
+ * 16-byte aligned; the values are meaningless).  *flops (host) receives the launch's
+ * matrix-core flops (16384 per product); divide by the launch's duration, timed by the caller
+ * on the same stream.  1 <= blocks <= 2^20, 1 <= iters <= 2^24, else HTA_ERR_SHAPE;
+ * HTA_ERR_NULL / HTA_ERR_ALIGN / HTA_ERR_HIP as for the other calls. */
+hta_status hta_mfma_peak_probe(int32_t blocks, int32_t iters, float *out, void *stream,
+                               double *flops);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *hta_status_str(hta_status status);
 

@@ -201,6 +201,16 @@ def test_other_entry_points_validate_before_launching():
     assert L.hta_get_device_status(ctypes.byref(d), None, None, None) == WORKSPACE
 
 
+def test_mfma_peak_probe_validates_before_launching():
+    L = hta.load()
+    f = ctypes.c_double(0.0)
+    assert L.hta_mfma_peak_probe(256, 16, None, None, ctypes.byref(f)) == NULL
+    assert L.hta_mfma_peak_probe(256, 16, 0x1000, None, None) == NULL
+    for blocks, iters in ((0, 16), (1 << 21, 16), (256, 0), (256, 1 << 25)):
+        assert L.hta_mfma_peak_probe(blocks, iters, 0x1000, None, ctypes.byref(f)) == SHAPE
+    assert L.hta_mfma_peak_probe(256, 16, 0x1004, None, ctypes.byref(f)) == ALIGN
+
+
 def test_version():
     assert hta.load().hta_version() >= 100
 

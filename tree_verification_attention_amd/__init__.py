@@ -38,6 +38,7 @@ from .binding import (  # noqa: F401
     prepare_chunk_mass,
     prepare_cross_attention,
     prepare_merge,
+    prepare_mfma_peak_probe,
     prepare_prefix_partials,
     prepare_rope_tree,
     prepare_tree_partials,
@@ -56,7 +57,8 @@ __all__ = [
     "hta_dense_mask", "hta_verify_dense", "verify_dense", "hta_get_device_status", "hta_merge",
     "hta_prefix_partials", "hta_rope_tree", "hta_tree_partials", "hta_verify", "hta_verify_noalloc", "load",
     "make_desc", "new_workspace", "partial_views", "plan", "prepare_accept_commit",
-    "prepare_chunk_mass", "prepare_cross_attention", "prepare_merge", "prepare_prefix_partials",
+    "prepare_chunk_mass", "prepare_cross_attention", "prepare_merge", "prepare_mfma_peak_probe",
+    "prepare_prefix_partials",
     "prepare_rope_tree", "prepare_tree_partials", "prepare_verify", "rope_tree", "status_str", "verify",
     "workspace_size",
 ]

@@ -52,6 +52,7 @@ EXPORTED = (
     "hta_accept_commit",
     "hta_status_str",
     "hta_version",
+    "hta_mfma_peak_probe",
 )
 
 
@@ -133,10 +134,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     L.hta_status_str.argtypes = [ctypes.c_int]
     L.hta_status_str.restype = ctypes.c_char_p
     L.hta_version.argtypes = []
+    L.hta_mfma_peak_probe.argtypes = [I, I, P, P, ctypes.POINTER(ctypes.c_double)]
     for f in (L.hta_plan, L.hta_verify, L.hta_verify_noalloc, L.hta_ancestor_masks, L.hta_prefix_partials,
               L.hta_tree_partials, L.hta_merge, L.hta_get_device_status, L.hta_version,
               L.hta_rope_tree, L.hta_accept_commit, L.hta_chunk_mass, L.hta_dense_mask,
-              L.hta_verify_dense, L.hta_cross_attention, L.hta_window_commit):
+              L.hta_verify_dense, L.hta_cross_attention, L.hta_window_commit,
+              L.hta_mfma_peak_probe):
         f.restype = ctypes.c_int
     _lib = L
     return L
@@ -632,6 +635,19 @@ def hta_accept_commit(desc, logits, tokens, root_token, parent_idx, prefix_len, 
     prepare_accept_commit(desc, logits, tokens, root_token, parent_idx, prefix_len, k_prefix,
                           v_prefix, k_tree, v_tree, target_next, accept_len, accepted,
                           bonus_token, workspace, stream)()
+
+
+def prepare_mfma_peak_probe(blocks: int, iters: int, out: torch.Tensor, stream=None):
+    """hta_mfma_peak_probe (a measurement helper, not part of the path) checked and marshalled
+    once: returns (call, flops per launch); the preparation enqueues one launch (a warm-up).
+    out: float32 on the GPU, blocks * 512 elements."""
+    _validate([("out", out, (int(blocks) * 512,), _F32)])
+    flops = ctypes.c_double(0.0)
+    fn = load().hta_mfma_peak_probe
+    args = (int(blocks), int(iters), _ptr(out), _stream(stream), ctypes.byref(flops))
+    call = _enqueue(fn, args, (out, flops), "hta_mfma_peak_probe")
+    call()
+    return call, float(flops.value)
 
 
 # ----------------------------------------------------------------------------- convenience
